@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention forward pass on one MI355X.
+
+One step = one call of the forward pass (the whole hot path is one kernel
+launch) on the headline workload B=8, H=32, N=2048, d=128, bf16, non-causal,
+scale 1/sqrt(d), inputs resident in HBM.  Prints ONE JSON line on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--all] [--copy-calibration BYTES]
+
+Throughput is counted as 4*B*H*N^2*d FLOPs per call (halved when causal).
+Timing uses HIP events recorded on the stream the kernel is launched on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (and % of MFMA peak) at N=2048,d=128 bf16"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}   # MI355X dense MFMA peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_63_amd", "csrc", f)
+                  for f in ("fa2_fwd_kernel.hpp", "fa2_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_gpu(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 CPU oracle timed on whole heads of the same workload until about
+    budget_s seconds of work are done (at least one head)."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = make_inputs(1, 8, w.N, w.d, w.dtype, w.seed, w.sigma, w.key_offset)
+    q64, k64, v64 = to_f64(q)[0], to_f64(k)[0], to_f64(v)[0]
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < 8:
+        oracle.attention_3pass(q64[heads], k64[heads], v64[heads], w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops_per_head = w.flops / (w.B * w.H)
+    return {"value": round(heads * flops_per_head / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (all {w.N} rows each) of {w.name}, fp64 NumPy "
+                      f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
+
+
+def run_workload(w, steps, warmup, variant=0):
+    import torch
+    import exact_attention_63_amd as fa2
+    from workloads import workload_inputs
+    q, k, v = (t.cuda() for t in workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+
+    def step():
+        fa2.forward(q, k, v, causal=w.causal, scale=w.scale, variant=variant, out=o, lse=lse)
+
+    ms, wall_ms = time_gpu(step, steps, warmup)
+    return ms, wall_ms
+
+
+def copy_calibration(nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--variant", type=int, default=0, help="tile variant (0 = tuned default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this forward pass is not sharded across GPUs "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    from workloads import HEADLINE, WORKLOADS
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    ms, wall_ms = run_workload(w, args.steps, args.warmup, args.variant)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(name)
+
+    if args.all:
+        print(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}", file=sys.stderr)
+        for other in WORKLOADS.values():
+            oms, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), args.variant)
+            t = other.flops / (oms * 1e-3) / 1e12
+            print(f"{other.name:36s} {oms:9.4f} {t:9.1f} {100 * t / PEAK_TFLOPS[other.dtype]:6.1f}%",
+                  file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, rounded to the dtype)",
+        "config": {**w.describe(), "variant": args.variant, "parallelism": "single GPU",
+                   "wall_ms_per_step": round(wall_ms, 5)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

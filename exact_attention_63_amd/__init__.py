@@ -1,0 +1,155 @@
+"""Exact attention forward (FlashAttention-2 style) on AMD MI355X.
+
+A thin ctypes binding over ``libfa2.so``, the C ABI declared in
+``include/fa2.h``.  PyTorch only provides device memory and the stream; every
+step of the computation runs in the library's HIP kernel.  There is no CPU
+fallback: when the library is missing or no GPU is present, calls raise.
+
+    from exact_attention_63_amd import forward
+    o, lse = forward(q, k, v, causal=False)        # q, k, v: [B, H, N, d] cuda fp16/bf16
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "forward", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
+    "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
+    "Fa2Error",
+]
+
+FA2_OK = 0
+FA2_ERR_NULL = -1
+FA2_ERR_SHAPE = -2
+FA2_ERR_UNSUPPORTED = -3
+FA2_ERR_ALIGN = -4
+FA2_ERR_ARG = -5
+FA2_ERR_ALIAS = -6
+FA2_ERR_LAUNCH = -7
+FA2_DTYPE_FP16 = 0
+FA2_DTYPE_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa2.so")
+_lib = None
+
+# argument lists of the exported functions (include/fa2.h)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_FWD12 = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]
+EXPORTS = {
+    "fa2_fwd_fp16": (_I, _FWD12),
+    "fa2_fwd_bf16": (_I, _FWD12),
+    "fa2_fwd": (_I, _FWD12 + [_I]),
+    "fa2_fwd_variant": (_I, _FWD12 + [_I, _I]),
+    "fa2_fwd_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+    "fa2_num_variants": (_I, []),
+    "fa2_variant_name": (ctypes.c_char_p, [_I]),
+    "fa2_status_string": (ctypes.c_char_p, [_I]),
+    "fa2_version": (_I, []),
+}
+
+
+class Fa2Error(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa2.so (built in-tree by ``python -m exact_attention_63_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m exact_attention_63_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback implementation")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa2_status_string(status).decode()
+
+
+def num_variants() -> int:
+    return lib().fa2_num_variants()
+
+
+def variant_name(variant: int) -> str | None:
+    s = lib().fa2_variant_name(variant)
+    return None if s is None else s.decode()
+
+
+def version() -> int:
+    return lib().fa2_version()
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype == torch.float16:
+        return FA2_DTYPE_FP16
+    if dtype == torch.bfloat16:
+        return FA2_DTYPE_BF16
+    raise ValueError(f"q, k, v must be float16 or bfloat16, got {dtype}")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, *, variant: int = 0,
+            out=None, lse=None):
+    """Attention forward: returns (O [B,H,N,d] in q's dtype, LSE [B,H,N] float32).
+
+    q, k, v: contiguous CUDA (ROCm) tensors [B, H, N, d] of one dtype (fp16 or
+    bf16), d in {64, 128}.  scale defaults to 1/sqrt(d).  The kernel is
+    enqueued on the current stream of q's device; the call does not
+    synchronise.  ``out`` / ``lse`` may pass preallocated outputs.
+    """
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one shape [B, H, N, d]; got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q.dtype)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib().fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, int(bool(causal)), float(scale),
+                                   stream, code, int(variant))
+    if rc != FA2_OK:
+        raise Fa2Error(rc, "fa2_fwd_variant")
+    return out, lse

@@ -1,0 +1,410 @@
+// fa2_fwd_kernel.hpp -- exact attention forward for gfx950 (CDNA4): one
+// workgroup per (query block, head, batch), sliced-Q over 64-lane waves,
+// online softmax in registers, both products on MFMA.
+//
+// Method: "FlashAttention v2 better parallelism + work partitioning" diagram.
+//   * grid over (batch, head, query block): the "parallel for batch, head,
+//     q_block" loop of the concept pseudo-code panel and the sequence-length
+//     parallelism of the "what v2 changes" panel;
+//   * the rows of a query block are split across the waves of the workgroup,
+//     each wave keeps its own (m, l, acc) and writes its own output rows, and
+//     the K/V tile is loaded once into shared memory for all waves (sliced-Q
+//     panel and the thread/data-movement panel);
+//   * per key tile: S = Q K^T, mask only where a mask can matter, online
+//     softmax update, acc += P V (concept pseudo-code panel);
+//   * final O = acc / l once at the end ("FlashAttention v4 Blackwell pipeline
+//     co-design" diagram, pseudo-code panel), so no per-tile divide.
+//
+// MI355X-specific design (none of this is on the pages, which target NVIDIA):
+//   * Scores are produced transposed, S^T = K Q^T, with the 32x32x16 MFMA.  In
+//     that layout a lane holds one query (lane % 32) and 16 keys per 32x32
+//     block, so the row max, the row sum and the rescale of acc by alpha are
+//     in-lane; only one exchange between lane l and lane l^32 is needed per
+//     row statistic.  The output is accumulated transposed too,
+//     O^T += V^T P^T, whose B operand (keys x queries) is exactly the S^T
+//     accumulator registers [8s, 8s+8) of each 16-key step s once keys are
+//     renumbered inside every 32-key block (slot 16s+8h+4a+b holds key
+//     16s+8a+4h+b).  P therefore never leaves registers.
+//   * K is staged row-major [key][d]; V is staged transposed [d][slot] with
+//     the slot renumbering above, so that both MFMA A operands are single
+//     16-byte LDS reads.  Every LDS row is padded by 16 bytes: the 8 (or 16)
+//     lanes served per LDS cycle read 8 (16) consecutive rows at one column,
+//     and a row pitch of 16 mod 128 (mod 256) bytes puts them on distinct
+//     banks (the bank-conflict fix of blog chapter 4, done with padding
+//     instead of an XOR swizzle so that every unrolled access is a constant
+//     offset from one per-lane base address).
+//   * Global reads and writes use buffer instructions with the head's extent
+//     as the range: rows past N read as zero and their stores are dropped, so
+//     ragged N needs no branches in the copy code.
+//   * Scale is folded into one FMA feeding exp2: p = 2^(s*c - m) with
+//     c = scale*log2(e) (blog chapter 6, FP instruction fusion); m, l are
+//     kept in the base-2 domain; LSE = (m + log2 l) * ln 2 at the end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+
+namespace fa2 {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <bool BF16>
+struct Elem;
+
+template <>
+struct Elem<true> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <>
+struct Elem<false> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// Wave-level exchange with the lane 32 positions away (lane l <-> l ^ 32).
+__device__ __forceinline__ float xchg32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+struct Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;      // B*H
+  int N;       // sequence length
+  int nqb;     // query blocks per head
+  float c;     // scale * log2(e)
+};
+
+// Tile configuration.
+//   NW : waves per workgroup         QB : 32-query blocks per wave
+//   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
+template <int NW_, int QB_, int KB_, int WPE_>
+struct Tile {
+  static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
+  static constexpr int BC = 32 * KB;       // keys per tile
+  static constexpr int THREADS = NW * 64;
+};
+
+template <bool BF16, int D, bool CAUSAL, class TL>
+__global__ __attribute__((amdgpu_flat_work_group_size(TL::THREADS, TL::THREADS),
+                          amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
+void fa2_fwd_kernel(Args a) {
+  using E = Elem<BF16>;
+  constexpr int NW = TL::NW, QB = TL::QB, KB = TL::KB;
+  constexpr int BR = TL::BR, BC = TL::BC, T = TL::THREADS;
+  constexpr int DK = D / 16;            // 16-wide k steps of the score product
+  constexpr int DB = D / 32;            // 32-row blocks of O^T
+  constexpr int KROW = D * 2;           // bytes per K (and Q, V, O) row in HBM
+  constexpr int KP = KROW + 16;         // padded K row pitch in LDS
+  constexpr int VP = BC * 2 + 16;       // padded V^T row pitch in LDS
+  constexpr int KSTAGE = BC * KP;       // bytes of one K tile
+  constexpr int VSTAGE = D * VP;        // bytes of one V^T tile
+  constexpr int STAGE = KSTAGE + VSTAGE;
+  constexpr int KCH = BC * D / 8;       // 16-byte chunks per K tile
+  constexpr int KCH_T = KCH / T;        // ... per thread
+  constexpr int VPAIRS = (BC / 4) * (D / 2);  // (4-key group, d pair) units per V tile
+  constexpr int VPAIRS_T = VPAIRS / T;
+  static_assert(KCH % T == 0 && VPAIRS % T == 0, "tile copy must split evenly over threads");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane & 31;   // query (S^T column) / row index inside a 32-block
+  const int lh = lane >> 5;   // which half of the 64-lane wave
+
+  // ---- workgroup -> (query block, head) --------------------------------
+  // Non-causal: all workgroups do equal work; consecutive logical ids walk the
+  // query blocks of one head and are kept on one XCD (workgroups are dealt to
+  // the 8 XCDs round-robin), so a head's K/V stay in that XCD's L2.
+  // Causal: heaviest query blocks first; with B*H a multiple of 8 each XCD
+  // then owns a fixed set of heads.
+  int bh, qblk;
+  {
+    const int i = blockIdx.x;
+    const int total = a.nqb * a.BH;
+    if constexpr (!CAUSAL) {
+      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+      bh = logical / a.nqb;
+      qblk = logical % a.nqb;
+    } else {
+      bh = i % a.BH;
+      qblk = a.nqb - 1 - i / a.BH;
+    }
+  }
+  const int N = a.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;   // elements
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.q + head_off), 0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.k + head_off), 0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint16_t*)a.v + head_off), 0, head_bytes, kBufferWord3);
+
+  const int q_wg = qblk * BR;                 // first query row of the workgroup
+  const int q_w = q_wg + wave * 32 * QB;      // first query row of this wave
+
+  // number of key tiles this workgroup visits
+  int nt = (N + BC - 1) / BC;
+  if constexpr (CAUSAL) {
+    const int last_row = min(q_wg + BR, N) - 1;
+    nt = min(nt, last_row / BC + 1);
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in VGPRs -------------
+  u32x4 qf[QB][DK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = q_w + qb * 32 + lr;
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      qf[qb][dk] = __builtin_amdgcn_raw_buffer_load_b128(qr, (uint32_t)(row * KROW + (2 * dk + lh) * 16), 0, 0);
+    }
+  }
+
+  // ---- staging registers for the next K/V tile ---------------------------
+  u32x4 kst[KCH_T];
+  uint32_t vst[VPAIRS_T][4];
+
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int it = 0; it < KCH_T; ++it) {
+      const int e = tid + it * T;
+      const int row = e / (D / 8), ch = e % (D / 8);
+      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (uint32_t)((key0 + row) * KROW + ch * 16), 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < VPAIRS_T; ++it) {
+      const int e = tid + it * T;
+      const int p = e % (D / 2), kg = e / (D / 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vst[it][r] = __builtin_amdgcn_raw_buffer_load_b32(vr, (uint32_t)((key0 + kg * 4 + r) * KROW + p * 4), 0, 0);
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    uint8_t* ks = smem + stage * STAGE;
+    uint8_t* vs = ks + KSTAGE;
+#pragma unroll
+    for (int it = 0; it < KCH_T; ++it) {
+      const int e = tid + it * T;
+      const int row = e / (D / 8), ch = e % (D / 8);
+      *(u32x4*)(ks + row * KP + ch * 16) = kst[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VPAIRS_T; ++it) {
+      const int e = tid + it * T;
+      const int p = e % (D / 2), kg = e / (D / 2);
+      // key group kg (4 keys) -> slot group: swap bits 0 and 1 inside each 16-key step
+      const int g = kg & 3;
+      const int sg = (kg & ~3) | ((g & 1) << 1) | (g >> 1);
+      const uint32_t* w = vst[it];
+      u32x2 lo, hi;
+      lo[0] = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+      const int d0 = 2 * p, d1 = 2 * p + 1;
+      *(u32x2*)(vs + d0 * VP + sg * 8) = lo;
+      *(u32x2*)(vs + d1 * VP + sg * 8) = hi;
+    }
+  };
+
+  // ---- per-row online-softmax state (base-2 domain) ----------------------
+  f32x16 acc[QB][DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+  }
+  const float c = a.c;
+  const bool c_nonneg = c >= 0.f;
+  const int kbase = lr * KP + lh * 16;   // this lane's K fragment: row 32*kb + lr, chunk 2*dk + lh
+  const int vbase = lr * VP + lh * 16;   // this lane's V^T fragment: row 32*db + lr, chunk 4*kb + 2*st + lh
+
+  auto compute = [&](int stage, int key0, bool masked) {
+    const uint8_t* ks = smem + stage * STAGE;
+    const uint8_t* vs = ks + KSTAGE;
+
+    // S^T = K Q^T for every (key block, query block)
+    f32x16 s[QB][KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 kf = *(const u32x4*)(ks + kbase + 32 * kb * KP + 32 * dk);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = E::mfma(kf, qf[qb][dk], s[qb][kb]);
+      }
+    }
+
+    // online softmax, one query per lane and query block
+    u32x4 pf[QB][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float cc = c;
+      float m_tile;
+      if (masked) {
+        // tiles that cross the diagonal or the end of the sequence: scale
+        // first, then masked scores are -inf and exp2 gives exactly 0
+        const int q = q_w + qb * 32 + lr;
+        float e = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const bool vis = key < N && (!CAUSAL || key <= q);
+            const float t = vis ? s[qb][kb][r] * c : -INFINITY;
+            s[qb][kb][r] = t;
+            e = fmaxf(e, t);
+          }
+        e = fmaxf(e, xchg32(e));
+        m_tile = e;
+        cc = 1.f;
+      } else if (c_nonneg) {
+        // max of c*s is c*max(s) for c >= 0 ...
+        float e = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e = fmaxf(e, s[qb][kb][r]);
+        e = fmaxf(e, xchg32(e));
+        m_tile = e * c;
+      } else {
+        // ... and c*min(s) for c < 0
+        float e = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e = fminf(e, s[qb][kb][r]);
+        e = fminf(e, xchg32(e));
+        m_tile = e * c;
+      }
+      const float m_new = fmaxf(m_run[qb], m_tile);
+      // a row with no visible key so far keeps m = -inf; never form -inf - -inf
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
+      m_run[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * st + t], cc, -m_use));
+            rs += p[t];
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) pf[qb][kb][st][t] = E::pack(p[2 * t], p[2 * t + 1]);
+        }
+      }
+      l_run[qb] = l_run[qb] * alpha + rs;
+      // rescale acc; exact skip when no row of the wave changed its max
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const u32x4 vf = *(const u32x4*)(vs + vbase + 32 * db * VP + (4 * kb + 2 * st) * 16);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mfma(vf, pf[qb][kb][st], acc[qb][db]);
+        }
+      }
+    }
+  };
+
+  // ---- main loop: 2-stage LDS ring, next tile's loads overlap compute ----
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int key0 = j * BC;
+    if (j + 1 < nt) load_tile(key0 + BC);
+    const bool skip = CAUSAL && key0 > q_w + 32 * QB - 1;       // tile entirely above the diagonal
+    const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
+    if (!skip) compute(j & 1, key0, masked);
+    if (j + 1 < nt) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ---------------------
+  const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)a.o + head_off), 0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t lr_ = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = q_w + qb * 32 + lr;
+    const float l = l_run[qb] + xchg32(l_run[qb]);
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = E::pack(acc[qb][db][4 * i + 0] * inv, acc[qb][db][4 * i + 1] * inv);
+        w[1] = E::pack(acc[qb][db][4 * i + 2] * inv, acc[qb][db][4 * i + 3] * inv);
+        const int d = 32 * db + 8 * i + 4 * lh;
+        __builtin_amdgcn_raw_buffer_store_b64(w, orr, (uint32_t)(row * KROW + d * 2), 0, 0);
+      }
+    }
+    if (lh == 0) {
+      const float lse = (m_run[qb] + log2f(l)) * 0.69314718055994530942f;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lr_, (uint32_t)(row * 4), 0, 0);
+    }
+  }
+}
+
+}  // namespace fa2

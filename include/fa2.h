@@ -1,0 +1,137 @@
+/*
+ * fa2.h -- C ABI of the exact-attention forward pass (FlashAttention-2 style)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every batch b, head h and query row i,
+ *
+ *     O[b,h,i,:] = sum_{j visible to i} softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) * V[b,h,j,:]
+ *     LSE[b,h,i] = ln sum_{j visible to i} exp(scale * Q[b,h,i,:] . K[b,h,j,:])
+ *
+ * where every key j is visible when causal == 0 and keys j <= i are visible
+ * when causal == 1.  This is standard softmax attention (search-result page on
+ * the FlashAttention-2 paper, snippet "0x01 Standard Self-Attention"), computed
+ * exactly but in tiles with an online softmax, without ever storing the N x N
+ * score matrix ("FlashAttention v2 better parallelism + work partitioning"
+ * diagram, concept pseudo-code panel; the same page states the method is exact
+ * and needs O(N) extra memory).  LSE is the natural-log log-sum-exp of the
+ * scaled, masked scores of each row; the pages do not define it, it is the
+ * per-row statistic a backward pass needs.
+ *
+ * Layouts.  q, k, v and o are contiguous row-major [B, H, N, d] tensors of the
+ * selected 16-bit dtype (fp16 or bf16; element (b,h,i,t) at offset
+ * ((b*H + h)*N + i)*d + t).  lse is a contiguous [B, H, N] float32 tensor.
+ * Query and key lengths are equal (self-attention shapes).  N need not be a
+ * multiple of any tile size.
+ *
+ * Arithmetic.  Both products run on the MFMA units with 16-bit inputs and
+ * fp32 accumulation; the softmax runs in fp32.  P is rounded to the input
+ * dtype (round-to-nearest-even) before the P.V product; the row sum is taken
+ * from the fp32 P.  O is written rounded to nearest even in the input dtype.
+ *
+ * Ownership and execution.  All tensor pointers are DEVICE pointers owned by
+ * the caller.  The library allocates no memory, frees nothing, keeps no
+ * pointer after returning and needs no workspace.  A call only enqueues work
+ * on `stream` (0 = the default stream) and returns; the caller synchronises.
+ * Results are deterministic: equal inputs give bitwise-equal outputs.  The
+ * functions are thread-safe.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; when a
+ * check fails nothing is launched, o and lse are left untouched and a negative
+ * status is returned.  Checks run in this order, the first failure wins:
+ * dtype / causal / scale / variant (FA2_ERR_ARG), negative sizes
+ * (FA2_ERR_SHAPE), empty problem (B, H or N == 0: FA2_OK, nothing is read or
+ * written and the pointers are not inspected), NULL pointers (FA2_ERR_NULL),
+ * d (FA2_ERR_UNSUPPORTED), size limits (FA2_ERR_SHAPE), alignment
+ * (FA2_ERR_ALIGN), overlap (FA2_ERR_ALIAS).  Faults that happen while the
+ * kernel runs surface at the caller's synchronisation, not here.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum fa2_status {
+    FA2_OK = 0,
+    FA2_ERR_NULL = -1,        /* a tensor pointer is NULL                                  */
+    FA2_ERR_SHAPE = -2,       /* B, H or N < 0, or a tensor or one head is too large       */
+    FA2_ERR_UNSUPPORTED = -3, /* d is not 64 or 128                                         */
+    FA2_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                    */
+    FA2_ERR_ARG = -5,         /* scale not finite, causal not 0/1, bad dtype or variant     */
+    FA2_ERR_ALIAS = -6,       /* o overlaps q, k, v or lse, or lse overlaps q, k or v       */
+    FA2_ERR_LAUNCH = -7       /* the HIP runtime reported an error when launching           */
+};
+
+/* Element type of q, k, v and o. */
+enum fa2_dtype {
+    FA2_DTYPE_FP16 = 0,
+    FA2_DTYPE_BF16 = 1
+};
+
+/*
+ * fa2_fwd_fp16 / fa2_fwd_bf16 -- the forward pass for one element type.
+ *
+ *   q, k, v  [in]  device, [B,H,N,d] fp16 (resp. bf16), 16-byte aligned
+ *   o        [out] device, [B,H,N,d] same dtype, 16-byte aligned, must not
+ *                  overlap any other argument
+ *   lse      [out] device, [B,H,N] float32, 16-byte aligned, must not overlap
+ *                  q, k, v or o
+ *   B, H, N        batch, heads, sequence length; each >= 0 (0 is a no-op).
+ *                  N*d*2 bytes (one head) must stay below 2^32 and B*H*N*d
+ *                  below 2^62.
+ *   d              head dimension: 64 or 128
+ *   causal         0: every key visible; 1: key j visible to query i iff j <= i
+ *   scale          multiplies q.k before the softmax; any finite value
+ *                  (0 gives uniform weights; negative values are allowed)
+ *   stream         HIP stream the kernel is enqueued on (0 = default stream)
+ *
+ * Returns FA2_OK or a negative fa2_status.
+ */
+int fa2_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+int fa2_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/* fa2_fwd -- the same twelve arguments plus dtype (an fa2_dtype value). */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, int causal, float scale, hipStream_t stream, int dtype);
+
+/*
+ * fa2_fwd_variant -- the forward pass with an explicit tile configuration,
+ * for tuning sweeps and tiling-invariance tests.  variant 0 is the tuned
+ * default that fa2_fwd uses; 1 .. fa2_num_variants()-1 select the entries
+ * described by fa2_variant_name().  Every variant computes the same function;
+ * results agree to rounding.  Returns FA2_ERR_ARG for an unknown variant.
+ */
+int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, int causal, float scale, hipStream_t stream,
+                    int dtype, int variant);
+
+/*
+ * fa2_fwd_check -- run exactly the argument validation of fa2_fwd_variant and
+ * return its status, without launching anything or calling the HIP runtime.
+ */
+int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  int B, int H, int N, int d, int causal, float scale, int dtype, int variant);
+
+/* Number of tile variants (including the default, 0). */
+int fa2_num_variants(void);
+
+/* Static description of a variant ("default" for 0), or NULL when out of range. */
+const char* fa2_variant_name(int variant);
+
+/* Static text for a status code; never NULL. */
+const char* fa2_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP forward pass against the fp64 CPU oracle.
+
+Tolerances (max over all compared elements, against the unrounded fp64
+oracle on the same rounded inputs): O within 2e-3 for fp16 and 1e-2 for bf16,
+LSE within 1e-3.  Small problems are compared element by element in full;
+the large workloads are compared on every row of some heads plus strided rows
+of all heads (rows are independent, so each checked row is an exact check),
+and through properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_63_amd as fa2
+import oracle
+from workloads import WORKLOADS, make_inputs, to_f64, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"fp16": 2e-3, "bf16": 1e-2}
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    fa2.lib()   # fails loudly when the library is missing
+
+
+def gpu_forward(q, k, v, causal, scale, variant=0):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = fa2.forward(qd, kd, vd, causal=causal, scale=scale, variant=variant)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    """max-abs parity with a diagnostic (max |O| and error in output ulps)."""
+    og = to_f64(o_gpu) if isinstance(o_gpu, torch.Tensor) else o_gpu
+    lg = to_f64(lse_gpu) if isinstance(lse_gpu, torch.Tensor) else lse_gpu
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), f"{what}: non-finite output"
+    eo = np.abs(og - o_ref).max() if og.size else 0.0
+    el = np.abs(lg - lse_ref).max() if lg.size else 0.0
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
+    scale = np.maximum(np.abs(o_ref), 2.0 ** -14)
+    worst_ulps = (np.abs(og - o_ref) / (ulp * 2.0 ** np.floor(np.log2(scale)))).max() if og.size else 0
+    msg = (f"{what}: max|dO|={eo:.3e} (tol {TOL_O[dtype]}), max|dLSE|={el:.3e} (tol {TOL_LSE}), "
+           f"max|O|={np.abs(o_ref).max() if og.size else 0:.3f}, worst {worst_ulps:.2f} ulp")
+    print(msg, flush=True)
+    assert eo <= TOL_O[dtype], msg
+    assert el <= TOL_LSE, msg
+
+
+def oracle_full(q, k, v, causal, scale):
+    return oracle.attention_3pass(to_f64(q), to_f64(k), to_f64(v), causal, scale)
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("name", ["b1h1n128d64_fp16", "b4h16n1024d64_fp16", "b4h16n1024d64_fp16_causal"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    o, lse = gpu_forward(q, k, v, w.causal, w.scale)
+    o_ref, l_ref = oracle_full(q, k, v, w.causal, w.scale)
+    check(o, lse, o_ref, l_ref, w.dtype, name)
+
+
+def sampled_rows(n, stride):
+    rows = np.unique(np.concatenate([np.arange(0, n, stride), np.arange(min(n, 64)), np.arange(max(0, n - 64), n)]))
+    return rows
+
+
+@pytest.mark.parametrize("name,full_heads,stride", [
+    ("b8h32n2048d128_bf16", [(0, 0), (7, 31), (3, 17)], 61),
+    ("b2h16n4096d128_bf16_causal", [(0, 0), (1, 15)], 127),
+    ("b1h32n16384d128_bf16_causal_koff", [(0, 0)], 509),
+])
+def test_workload_sampled(name, full_heads, stride):
+    """Full-size launch (the configuration the benchmark times); every row of
+    some heads and strided rows of every head against the oracle."""
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    o, lse = gpu_forward(q, k, v, w.causal, w.scale)
+    o64, l64 = to_f64(o), to_f64(lse)
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    for b, h in full_heads:
+        o_ref, l_ref = oracle.attention_3pass(q64[b, h], k64[b, h], v64[b, h], w.causal, w.scale)
+        check(o64[b, h], l64[b, h], o_ref, l_ref, w.dtype, f"{name} head ({b},{h}) all rows")
+    rows = sampled_rows(w.N, stride)
+    o_ref, l_ref = oracle.attention_3pass(q64, k64, v64, w.causal, w.scale, rows=rows)
+    check(o64[:, :, rows], l64[:, :, rows], o_ref, l_ref, w.dtype, f"{name} {rows.size} rows x all heads")
+
+
+# ------------------------------------------------------------ edge shapes
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129, 1000])
+def test_edge_shapes(N, d, causal, dtype):
+    seed = 10_000 + N * 8 + (d == 128) * 4 + causal * 2 + (dtype == "bf16")
+    q, k, v = make_inputs(1, 2, N, d, dtype, seed)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    o_ref, l_ref = oracle_full(q, k, v, causal, scale)
+    check(o, lse, o_ref, l_ref, dtype, f"N={N} d={d} causal={causal} {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, 1.0, -0.5, 0.3])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scales(scale, d, causal):
+    q, k, v = make_inputs(2, 2, 200, d, "bf16", seed=77 + d)
+    o, lse = gpu_forward(q, k, v, causal, scale)
+    o_ref, l_ref = oracle_full(q, k, v, causal, scale)
+    check(o, lse, o_ref, l_ref, "bf16", f"scale={scale} d={d} causal={causal}")
+
+
+def test_large_logit_range_fp16():
+    """scale = 1 at d = 128 makes logits ~ N(0, 128): constant max jumps."""
+    q, k, v = make_inputs(1, 4, 777, 128, "fp16", seed=5)
+    o, lse = gpu_forward(q, k, v, True, 1.0)
+    o_ref, l_ref = oracle_full(q, k, v, True, 1.0)
+    check(o, lse, o_ref, l_ref, "fp16", "scale=1 d=128 fp16 causal")
+
+
+# ------------------------------------------------------------ tile variants
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(64, "fp16"), (128, "bf16")])
+def test_every_variant_matches_oracle(causal, d, dtype):
+    q, k, v = make_inputs(2, 3, 1000, d, dtype, seed=31)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, l_ref = oracle_full(q, k, v, causal, scale)
+    outs = []
+    for vi in range(fa2.num_variants()):
+        o, lse = gpu_forward(q, k, v, causal, scale, variant=vi)
+        check(o, lse, o_ref, l_ref, dtype, f"variant {vi} ({fa2.variant_name(vi)})")
+        outs.append((to_f64(o), to_f64(lse)))
+    # tiling invariance: variants agree with each other to within rounding
+    for o_i, l_i in outs[1:]:
+        assert np.abs(o_i - outs[0][0]).max() <= 2 * TOL_O[dtype]
+        assert np.abs(l_i - outs[0][1]).max() <= 2 * TOL_LSE
+
+
+# ------------------------------------------------------------ properties
+
+def test_deterministic_full_size():
+    w = WORKLOADS["b8h32n2048d128_bf16"]
+    q, k, v = (t.cuda() for t in workload_inputs(w))
+    o1, l1 = fa2.forward(q, k, v, causal=False)
+    o2, l2 = fa2.forward(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_constant_v_full_size():
+    """V rows all equal c  =>  O rows equal c (softmax weights sum to one)."""
+    w = WORKLOADS["b8h32n2048d128_bf16"]
+    q, k, _ = workload_inputs(w)
+    c = torch.randn(w.d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    v = c.expand(w.B, w.H, w.N, w.d).contiguous()
+    o, _ = gpu_forward(q, k, v, False, w.scale)
+    err = (o.float().cpu() - c.float()).abs().max().item()
+    assert err <= TOL_O["bf16"], err
+
+
+def test_causal_row0_full_size():
+    """causal row 0 sees only key 0: O[0] = V[0] exactly, LSE[0] = scale q0.k0."""
+    w = WORKLOADS["b1h32n16384d128_bf16_causal_koff"]
+    q, k, v = workload_inputs(w)
+    o, lse = gpu_forward(q, k, v, True, w.scale)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+    q0 = to_f64(q[:, :, 0])
+    k0 = to_f64(k[:, :, 0])
+    ref = w.scale * (q0 * k0).sum(-1)
+    assert np.abs(to_f64(lse[:, :, 0]) - ref).max() <= TOL_LSE
+
+
+def test_outputs_fully_written():
+    q, k, v = (t.cuda() for t in make_inputs(2, 3, 1000, 128, "bf16", seed=9))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((2, 3, 1000), float("nan"), device="cuda")
+    fa2.forward(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_row_independence():
+    """Changing query row r changes only O[r] and LSE[r] (sliced-Q: no
+    reduction across rows)."""
+    q, k, v = (t.cuda() for t in make_inputs(1, 2, 300, 64, "fp16", seed=4))
+    o1, l1 = fa2.forward(q, k, v, causal=True)
+    q2 = q.clone()
+    q2[:, :, 17] = -q2[:, :, 17]
+    o2, l2 = fa2.forward(q2, k, v, causal=True)
+    torch.cuda.synchronize()
+    keep = torch.ones(300, dtype=torch.bool)
+    keep[17] = False
+    assert torch.equal(o1[:, :, keep], o2[:, :, keep]) and torch.equal(l1[:, :, keep], l2[:, :, keep])
+    assert not torch.equal(o1[:, :, 17], o2[:, :, 17])
+
+
+def test_self_attention_shared_input():
+    x, _, _ = make_inputs(1, 2, 333, 64, "bf16", seed=12)
+    o, lse = gpu_forward(x, x, x, True, 0.125)
+    o_ref, l_ref = oracle_full(x, x, x, True, 0.125)
+    check(o, lse, o_ref, l_ref, "bf16", "q = k = v")
+
+
+def test_side_stream():
+    q, k, v = (t.cuda() for t in make_inputs(1, 2, 256, 128, "fp16", seed=13))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa2.forward(q, k, v, causal=False)
+    s.synchronize()
+    o_ref, l_ref = oracle_full(q.cpu(), k.cpu(), v.cpu(), False, 1 / math.sqrt(128))
+    check(o, lse, o_ref, l_ref, "fp16", "side stream")
+
+
+def test_errors_with_device_tensors():
+    q, k, v = (t.cuda() for t in make_inputs(1, 1, 64, 64, "bf16", seed=1))
+    with pytest.raises(fa2.Fa2Error) as ei:
+        fa2.forward(q, k, v, out=q)
+    assert ei.value.status == fa2.FA2_ERR_ALIAS
+    flat = torch.empty(64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    mis = flat[1:].view(1, 1, 64, 64)
+    mis.copy_(q)
+    with pytest.raises(fa2.Fa2Error) as ei:
+        fa2.forward(mis, k, v)
+    assert ei.value.status == fa2.FA2_ERR_ALIGN
+    q32 = torch.zeros(1, 1, 64, 32, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa2.Fa2Error) as ei:
+        fa2.forward(q32, q32, q32)
+    assert ei.value.status == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_empty_sequence():
+    q = torch.empty(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    o, lse = fa2.forward(q, q, q)
+    assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
