@@ -19,20 +19,22 @@
 //   * Scores are produced transposed, S^T = K Q^T, with the 32x32x16 MFMA.  In
 //     that layout a lane holds one query (lane % 32) and 16 keys per 32x32
 //     block, so the row max, the row sum and the rescale of acc by alpha are
-//     in-lane; only one exchange between lane l and lane l^32 is needed per
-//     row statistic.  The output is accumulated transposed too,
+//     in-lane; only one exchange between lane l and lane l^32
+//     (v_permlane32_swap) is needed per row statistic.  The output is accumulated transposed too,
 //     O^T += V^T P^T, whose B operand (keys x queries) is exactly the S^T
 //     accumulator registers [8s, 8s+8) of each 16-key step s once keys are
 //     renumbered inside every 32-key block (slot 16s+8h+4a+b holds key
 //     16s+8a+4h+b).  P therefore never leaves registers.
-//   * K is staged row-major [key][d]; V is staged transposed [d][slot] with
-//     the slot renumbering above, so that both MFMA A operands are single
-//     16-byte LDS reads.  Every LDS row is padded by 16 bytes: the 8 (or 16)
-//     lanes served per LDS cycle read 8 (16) consecutive rows at one column,
-//     and a row pitch of 16 mod 128 (mod 256) bytes puts them on distinct
-//     banks (the bank-conflict fix of blog chapter 4, done with padding
-//     instead of an XOR swizzle so that every unrolled access is a constant
-//     offset from one per-lane base address).
+//   * K and V are both staged row-major [key][d].  K fragments are 16-byte
+//     LDS reads; V^T fragments (keys along the MFMA k dimension) come from
+//     the gfx950 LDS transpose read ds_read_b64_tr_b16, whose lane mapping
+//     also realises the key renumbering above, so V needs no transpose in
+//     registers.  LDS rows are padded so that the lanes one LDS cycle serves
+//     fall on distinct banks: K pitch = 16 mod 128 bytes (16-byte reads of 8
+//     consecutive rows), V pitch = 32 mod 128 bytes (32-byte runs of 4
+//     consecutive rows) -- the bank-conflict fix of blog chapter 4, done with
+//     padding instead of an XOR swizzle so that every unrolled access is a
+//     constant offset from one per-lane base address.
 //   * Global reads and writes use buffer instructions with the head's extent
 //     as the range: rows past N read as zero and their stores are dropped, so
 //     ragged N needs no branches in the copy code.
@@ -57,6 +59,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Buffer descriptor word 3 for raw (untyped) buffer access on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <bool BF16>
 struct Elem;
@@ -86,9 +90,31 @@ struct Elem<false> {
   }
 };
 
-// Wave-level exchange with the lane 32 positions away (lane l <-> l ^ 32).
-__device__ __forceinline__ float xchg32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a per-lane value with the one held 32 lanes away, leaving the
+// result in both lanes.  v_permlane32_swap(x, x) returns {x of lanes 0-31 in
+// both halves, x of lanes 32-63 in both halves}: one VALU op, no LDS.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float min_halves(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fminf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+
+// ds_read_b64_tr_b16: transpose read of 16-bit elements (see the V fragment
+// comment in the kernel for the lane mapping).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 struct Args {
@@ -124,16 +150,14 @@ void fa2_fwd_kernel(Args a) {
   constexpr int DK = D / 16;            // 16-wide k steps of the score product
   constexpr int DB = D / 32;            // 32-row blocks of O^T
   constexpr int KROW = D * 2;           // bytes per K (and Q, V, O) row in HBM
-  constexpr int KP = KROW + 16;         // padded K row pitch in LDS
-  constexpr int VP = BC * 2 + 16;       // padded V^T row pitch in LDS
+  constexpr int KP = KROW + 16;         // K row pitch in LDS (16 mod 128: 16-byte reads of 8 rows)
+  constexpr int VP = KROW + 32;         // V row pitch in LDS (32 mod 128: 32-byte runs of 4 rows)
   constexpr int KSTAGE = BC * KP;       // bytes of one K tile
-  constexpr int VSTAGE = D * VP;        // bytes of one V^T tile
+  constexpr int VSTAGE = BC * VP;       // bytes of one V tile
   constexpr int STAGE = KSTAGE + VSTAGE;
-  constexpr int KCH = BC * D / 8;       // 16-byte chunks per K tile
-  constexpr int KCH_T = KCH / T;        // ... per thread
-  constexpr int VPAIRS = (BC / 4) * (D / 2);  // (4-key group, d pair) units per V tile
-  constexpr int VPAIRS_T = VPAIRS / T;
-  static_assert(KCH % T == 0 && VPAIRS % T == 0, "tile copy must split evenly over threads");
+  constexpr int CH = BC * D / 8;        // 16-byte chunks per K (or V) tile
+  constexpr int CH_T = CH / T;          // ... per thread
+  static_assert(CH % T == 0, "tile copy must split evenly over threads");
   static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
@@ -195,24 +219,18 @@ void fa2_fwd_kernel(Args a) {
   }
 
   // ---- staging registers for the next K/V tile ---------------------------
-  u32x4 kst[KCH_T];
-  uint32_t vst[VPAIRS_T][4];
+  // Thread tid copies 16-byte chunks tid, tid + T, ... of each tile; a row of
+  // d elements is d/8 consecutive chunks, so a wave reads whole rows.
+  u32x4 kst[CH_T], vst[CH_T];
 
   auto load_tile = [&](int key0) {
 #pragma unroll
-    for (int it = 0; it < KCH_T; ++it) {
+    for (int it = 0; it < CH_T; ++it) {
       const int e = tid + it * T;
       const int row = e / (D / 8), ch = e % (D / 8);
-      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (uint32_t)((key0 + row) * KROW + ch * 16), 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < VPAIRS_T; ++it) {
-      const int e = tid + it * T;
-      const int p = e % (D / 2), kg = e / (D / 2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vst[it][r] = __builtin_amdgcn_raw_buffer_load_b32(vr, (uint32_t)((key0 + kg * 4 + r) * KROW + p * 4), 0, 0);
-      }
+      const uint32_t off = (uint32_t)((key0 + row) * KROW + ch * 16);
+      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      vst[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
     }
   };
 
@@ -220,27 +238,11 @@ void fa2_fwd_kernel(Args a) {
     uint8_t* ks = smem + stage * STAGE;
     uint8_t* vs = ks + KSTAGE;
 #pragma unroll
-    for (int it = 0; it < KCH_T; ++it) {
+    for (int it = 0; it < CH_T; ++it) {
       const int e = tid + it * T;
       const int row = e / (D / 8), ch = e % (D / 8);
       *(u32x4*)(ks + row * KP + ch * 16) = kst[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VPAIRS_T; ++it) {
-      const int e = tid + it * T;
-      const int p = e % (D / 2), kg = e / (D / 2);
-      // key group kg (4 keys) -> slot group: swap bits 0 and 1 inside each 16-key step
-      const int g = kg & 3;
-      const int sg = (kg & ~3) | ((g & 1) << 1) | (g >> 1);
-      const uint32_t* w = vst[it];
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-      const int d0 = 2 * p, d1 = 2 * p + 1;
-      *(u32x2*)(vs + d0 * VP + sg * 8) = lo;
-      *(u32x2*)(vs + d1 * VP + sg * 8) = hi;
+      *(u32x4*)(vs + row * VP + ch * 16) = vst[it];
     }
   };
 
@@ -257,7 +259,13 @@ void fa2_fwd_kernel(Args a) {
   const float c = a.c;
   const bool c_nonneg = c >= 0.f;
   const int kbase = lr * KP + lh * 16;   // this lane's K fragment: row 32*kb + lr, chunk 2*dk + lh
-  const int vbase = lr * VP + lh * 16;   // this lane's V^T fragment: row 32*db + lr, chunk 4*kb + 2*st + lh
+  // V^T fragments come from row-major V through the LDS transpose read.  In
+  // each 16-lane group g, lane (4e + c) fetches 4 elements of key row
+  // 4*(g/2) + e at columns 16*(g%2) + 4c; the hardware hands lane i of the
+  // group element i of each of the group's 4 rows, which is the A operand
+  // layout (d = lane % 32, keys 4*(lane/32) + 0..3 of the renumbered step).
+  const int vg = lane >> 4;
+  const int vbase = (4 * (vg >> 1) + ((lane >> 2) & 3)) * VP + 32 * (vg & 1) + 8 * (lane & 3);
 
   auto compute = [&](int stage, int key0, bool masked) {
     const uint8_t* ks = smem + stage * STAGE;
@@ -300,8 +308,7 @@ void fa2_fwd_kernel(Args a) {
             s[qb][kb][r] = t;
             e = fmaxf(e, t);
           }
-        e = fmaxf(e, xchg32(e));
-        m_tile = e;
+        m_tile = max_halves(e);
         cc = 1.f;
       } else if (c_nonneg) {
         // max of c*s is c*max(s) for c >= 0 ...
@@ -310,8 +317,7 @@ void fa2_fwd_kernel(Args a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) e = fmaxf(e, s[qb][kb][r]);
-        e = fmaxf(e, xchg32(e));
-        m_tile = e * c;
+        m_tile = max_halves(e) * c;
       } else {
         // ... and c*min(s) for c < 0
         float e = s[qb][0][0];
@@ -319,8 +325,7 @@ void fa2_fwd_kernel(Args a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) e = fminf(e, s[qb][kb][r]);
-        e = fminf(e, xchg32(e));
-        m_tile = e * c;
+        m_tile = min_halves(e) * c;
       }
       const float m_new = fmaxf(m_run[qb], m_tile);
       // a row with no visible key so far keeps m = -inf; never form -inf - -inf
@@ -357,7 +362,10 @@ void fa2_fwd_kernel(Args a) {
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const u32x4 vf = *(const u32x4*)(vs + vbase + 32 * db * VP + (4 * kb + 2 * st) * 16);
+          const uint8_t* vp = vs + vbase + (32 * kb + 16 * st) * VP + 64 * db;
+          const u32x2 lo = lds_read_tr16(vp);            // keys 4h + 0..3 of the step
+          const u32x2 hi = lds_read_tr16(vp + 8 * VP);   // keys 8 + 4h + 0..3
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mfma(vf, pf[qb][kb][st], acc[qb][db]);
         }
@@ -368,6 +376,11 @@ void fa2_fwd_kernel(Args a) {
   // ---- main loop: 2-stage LDS ring, next tile's loads overlap compute ----
   load_tile(0);
   store_tile(0);
+  // Every load issued so far (Q fragments, first tile) is complete here.
+  // Saying so explicitly keeps the compiler from placing waits for the Q
+  // loads inside the loop, where they would also wait for the prefetch of
+  // the next tile and expose its latency on every iteration.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   for (int j = 0; j < nt; ++j) {
     const int key0 = j * BC;
@@ -387,7 +400,7 @@ void fa2_fwd_kernel(Args a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = q_w + qb * 32 + lr;
-    const float l = l_run[qb] + xchg32(l_run[qb]);
+    const float l = sum_halves(l_run[qb]);
     const float inv = 1.f / l;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -38,6 +38,10 @@ READINGS where the pages are silent, garbled or ambiguous:
   R4  The scale multiplies the scores after the product (Q is never pre-scaled).
   R5  A tile with no visible key for a row leaves that row's state unchanged
       (exp offsets are guarded so that -inf - (-inf) never occurs).
+  R6  The conditional rescale of the v4 diagram ("skip the rescale when the
+      max changes little") is taken in its exact form: the reference max may
+      lag the true running max by at most a threshold; the final O and LSE
+      are unchanged in exact arithmetic.
 
 Pins that tie this module to something other than itself live in
 ``tests/test_oracle_pins.py``: brute-force sums on tiny inputs, the worked
@@ -147,7 +151,8 @@ def attention_3pass(q, k, v, causal: bool, scale: float, rows=None, chunk: int =
     return o.reshape(*lead, rows.size, d), lse.reshape(*lead, rows.size)
 
 
-def attention_online(q, k, v, causal: bool, scale: float, bc: int, trace=None):
+def attention_online(q, k, v, causal: bool, scale: float, bc: int, trace=None,
+                     rescale_threshold: float | None = None):
     """Tiled online-softmax model of the same forward pass, float64, one head.
 
     This is the update the GPU kernel implements, written in the order of the
@@ -163,6 +168,14 @@ def attention_online(q, k, v, causal: bool, scale: float, bc: int, trace=None):
 
     q, k, v: float64 [N, d].  trace: optional callable(j0, m, l, acc) called
     after every tile with copies of the state, for worked-example tests.
+
+    rescale_threshold (reading R6): when given as tau >= 0, the reference m of
+    a row moves to the new maximum only when that maximum exceeds m by more
+    than tau (or m is still -inf); otherwise m stays, alpha = 1 and the new
+    p = exp(s - m) may exceed 1 (by at most e^tau).  O = acc / l and
+    LSE = m + ln l use the same reference, so the result is the same exact
+    value; only the point at which acc and l are rescaled changes (the
+    conditional rescale of the FlashAttention v4 diagram, in its exact form).
     Returns (O [N, d], LSE [N]).
     """
     q = _as_f64(q)
@@ -184,6 +197,9 @@ def attention_online(q, k, v, causal: bool, scale: float, bc: int, trace=None):
         vis = visible_mask(rows, j1, causal)[:, j0:j1]
         s = np.where(vis, s, -np.inf)
         m_new = np.maximum(m, s.max(axis=1))
+        if rescale_threshold is not None:
+            keep = np.isfinite(m) & (m_new - m <= rescale_threshold)
+            m_new = np.where(keep, m, m_new)
         dead = np.isneginf(m_new)                     # no visible key yet
         ref = np.where(dead, 0.0, m_new)              # guarded subtrahend
         alpha = np.where(dead, 1.0, np.exp(m - ref))

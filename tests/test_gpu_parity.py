@@ -37,20 +37,39 @@ def gpu_forward(q, k, v, causal, scale, variant=0):
     return o, lse
 
 
-def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
-    """max-abs parity with a diagnostic (max |O| and error in output ulps)."""
+def half_ulp(x, dtype):
+    """Half an ulp of the output dtype at |x| (bf16: 8 significant bits, fp16: 11)."""
+    bits = 8 if dtype == "bf16" else 11
+    mag = np.maximum(np.abs(x), 2.0 ** -14)
+    return 2.0 ** (np.floor(np.log2(mag)) - bits)
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", output_rounding=False):
+    """max-abs parity, with a diagnostic (max |O|, worst error in output ulps).
+
+    output_rounding=True (stress cases beyond the specified workloads, whose
+    |O| can reach 4 and more) allows each element, on top of the tolerance,
+    the half ulp that storing the exact result in the output dtype costs by
+    itself: at |O| in [4, 8) that alone is 2^-6 = 0.0156 in bf16, above the
+    1e-2 bar.
+    """
     og = to_f64(o_gpu) if isinstance(o_gpu, torch.Tensor) else o_gpu
     lg = to_f64(lse_gpu) if isinstance(lse_gpu, torch.Tensor) else lse_gpu
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), f"{what}: non-finite output"
-    eo = np.abs(og - o_ref).max() if og.size else 0.0
-    el = np.abs(lg - lse_ref).max() if lg.size else 0.0
-    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
-    scale = np.maximum(np.abs(o_ref), 2.0 ** -14)
-    worst_ulps = (np.abs(og - o_ref) / (ulp * 2.0 ** np.floor(np.log2(scale)))).max() if og.size else 0
+    if og.size == 0:
+        return
+    err = np.abs(og - o_ref)
+    eo = err.max()
+    el = np.abs(lg - lse_ref).max()
+    ulps = (err / (2 * half_ulp(o_ref, dtype))).max()
     msg = (f"{what}: max|dO|={eo:.3e} (tol {TOL_O[dtype]}), max|dLSE|={el:.3e} (tol {TOL_LSE}), "
-           f"max|O|={np.abs(o_ref).max() if og.size else 0:.3f}, worst {worst_ulps:.2f} ulp")
+           f"max|O|={np.abs(o_ref).max():.3f}, worst {ulps:.2f} ulp")
     print(msg, flush=True)
-    assert eo <= TOL_O[dtype], msg
+    if output_rounding:
+        excess = (err - TOL_O[dtype] - half_ulp(o_ref, dtype)).max()
+        assert excess <= 0, msg
+    else:
+        assert eo <= TOL_O[dtype], msg
     assert el <= TOL_LSE, msg
 
 
@@ -117,7 +136,7 @@ def test_scales(scale, d, causal):
     q, k, v = make_inputs(2, 2, 200, d, "bf16", seed=77 + d)
     o, lse = gpu_forward(q, k, v, causal, scale)
     o_ref, l_ref = oracle_full(q, k, v, causal, scale)
-    check(o, lse, o_ref, l_ref, "bf16", f"scale={scale} d={d} causal={causal}")
+    check(o, lse, o_ref, l_ref, "bf16", f"scale={scale} d={d} causal={causal}", output_rounding=True)
 
 
 def test_large_logit_range_fp16():
@@ -125,7 +144,7 @@ def test_large_logit_range_fp16():
     q, k, v = make_inputs(1, 4, 777, 128, "fp16", seed=5)
     o, lse = gpu_forward(q, k, v, True, 1.0)
     o_ref, l_ref = oracle_full(q, k, v, True, 1.0)
-    check(o, lse, o_ref, l_ref, "fp16", "scale=1 d=128 fp16 causal")
+    check(o, lse, o_ref, l_ref, "fp16", "scale=1 d=128 fp16 causal", output_rounding=True)
 
 
 # ------------------------------------------------------------ tile variants
@@ -209,7 +228,7 @@ def test_self_attention_shared_input():
     x, _, _ = make_inputs(1, 2, 333, 64, "bf16", seed=12)
     o, lse = gpu_forward(x, x, x, True, 0.125)
     o_ref, l_ref = oracle_full(x, x, x, True, 0.125)
-    check(o, lse, o_ref, l_ref, "bf16", "q = k = v")
+    check(o, lse, o_ref, l_ref, "bf16", "q = k = v", output_rounding=True)
 
 
 def test_side_stream():

@@ -220,6 +220,34 @@ def test_online_equals_3pass(n, d, causal):
         np.testing.assert_allclose(lse, l3, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("tau", [0.0, 0.5, 3.0, 8.0 * math.log(2.0)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_lazy_rescale_is_exact(tau, causal):
+    """A reference max that lags the running max by <= tau gives the same O, LSE."""
+    rng = np.random.default_rng(2024)
+    q, k, v = rand_head(rng, 97, 16, sigma=1.5)
+    k = k + rng.uniform(-4, 4, size=(97, 1))       # per-key offsets: frequent max jumps
+    o3, l3 = attn3(q, k, v, causal, 0.5)
+    for bc in (1, 7, 32):
+        o, lse = oracle.attention_online(q, k, v, causal, 0.5, bc, rescale_threshold=tau)
+        np.testing.assert_allclose(o, o3, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l3, rtol=0, atol=1e-12)
+
+
+def test_lazy_rescale_keeps_reference_within_threshold():
+    """With the threshold, m never trails the true running max by more than tau."""
+    rng = np.random.default_rng(7)
+    q, k, v = rand_head(rng, 40, 8, sigma=2.0)
+    tau = 2.0
+    seen = []
+    oracle.attention_online(q, k, v, False, 1.0, 4, rescale_threshold=tau,
+                            trace=lambda j0, m, l, acc: seen.append((j0, m)))
+    s = q @ k.T
+    for j0, m in seen:
+        true_max = s[:, : j0 + 4].max(axis=1)
+        assert np.all(m <= true_max + 1e-12) and np.all(true_max - m <= tau + 1e-12)
+
+
 def test_online_state_matches_golden_steps():
     ex = load_golden()
     for name, e in ex.items():
