@@ -30,11 +30,12 @@
 //     the gfx950 LDS transpose read ds_read_b64_tr_b16, whose lane mapping
 //     also realises the key renumbering above, so V needs no transpose in
 //     registers.  LDS rows are padded so that the lanes one LDS cycle serves
-//     fall on distinct banks: K pitch = 16 mod 128 bytes (16-byte reads of 8
-//     consecutive rows), V pitch = 32 mod 128 bytes (32-byte runs of 4
-//     consecutive rows) -- the bank-conflict fix of blog chapter 4, done with
-//     padding instead of an XOR swizzle so that every unrolled access is a
-//     constant offset from one per-lane base address.
+//     fall on distinct banks of the 64 x 4-byte bank array: K pitch = 16 mod
+//     256 bytes (16-byte reads of 16 consecutive rows), V pitch = 64 mod 256
+//     bytes (transpose reads serve 32 lanes = 4 rows x 64 bytes per cycle) --
+//     the bank-conflict fix of blog chapter 4, done with padding instead of
+//     an XOR swizzle so that every unrolled access is a constant offset from
+//     one per-lane base address.
 //   * Global reads and writes use buffer instructions with the head's extent
 //     as the range: rows past N read as zero and their stores are dropped, so
 //     ragged N needs no branches in the copy code.
@@ -45,6 +46,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 
 namespace fa2 {
@@ -61,6 +64,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferWord3 = 0x00020000;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Lazy rescale threshold in base-2 units: p never exceeds 2^8 = 256.
+constexpr float kLazyRescale = 8.f;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+// VALU instructions placed after each score MFMA in the interleaved loop.
+constexpr int kValuPerMfma = 8;
 
 template <bool BF16>
 struct Elem;
@@ -98,11 +107,6 @@ __device__ __forceinline__ float max_halves(float x) {
                                                   __builtin_bit_cast(uint32_t, x), false, false);
   return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
 }
-__device__ __forceinline__ float min_halves(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return fminf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
-}
 __device__ __forceinline__ float sum_halves(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
@@ -132,9 +136,16 @@ struct Args {
 // Tile configuration.
 //   NW : waves per workgroup         QB : 32-query blocks per wave
 //   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
-template <int NW_, int QB_, int KB_, int WPE_>
+//   PIPE: software-pipelined main loop (see below)
+template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0>
 struct Tile {
   static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  // PIPE 1: issue the next tile's score MFMAs in the same basic block as the
+  // current tile's softmax (K staged two tiles ahead, V one tile ahead);
+  // PIPE 2: additionally ask the scheduler to interleave those MFMAs with the
+  // softmax VALU work one by one, so that one wave keeps both pipes busy;
+  // PIPE 3: ping-pong between two wave groups in opposite phases.
+  static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
   static constexpr int THREADS = NW * 64;
@@ -151,10 +162,10 @@ void fa2_fwd_kernel(Args a) {
   constexpr int DB = D / 32;            // 32-row blocks of O^T
   constexpr int KROW = D * 2;           // bytes per K (and Q, V, O) row in HBM
   constexpr int KP = KROW + 16;         // K row pitch in LDS (16 mod 128: 16-byte reads of 8 rows)
-  constexpr int VP = KROW + 32;         // V row pitch in LDS (32 mod 128: 32-byte runs of 4 rows)
+  constexpr int VP = KROW + 64;         // V row pitch in LDS (64 mod 256: 64-byte runs of 4 rows)
   constexpr int KSTAGE = BC * KP;       // bytes of one K tile
   constexpr int VSTAGE = BC * VP;       // bytes of one V tile
-  constexpr int STAGE = KSTAGE + VSTAGE;
+  constexpr int STAGE = KSTAGE + VSTAGE;  // LDS: K stage 0, K stage 1, V stage 0, V stage 1
   constexpr int CH = BC * D / 8;        // 16-byte chunks per K (or V) tile
   constexpr int CH_T = CH / T;          // ... per thread
   static_assert(CH % T == 0, "tile copy must split evenly over threads");
@@ -222,27 +233,39 @@ void fa2_fwd_kernel(Args a) {
   // Thread tid copies 16-byte chunks tid, tid + T, ... of each tile; a row of
   // d elements is d/8 consecutive chunks, so a wave reads whole rows.
   u32x4 kst[CH_T], vst[CH_T];
+  uint8_t* const kring = smem;                 // K stages 0, 1
+  uint8_t* const vring = smem + 2 * KSTAGE;    // V stages 0, 1
 
-  auto load_tile = [&](int key0) {
+  auto load_k = [&](int key0) {
 #pragma unroll
     for (int it = 0; it < CH_T; ++it) {
       const int e = tid + it * T;
       const int row = e / (D / 8), ch = e % (D / 8);
-      const uint32_t off = (uint32_t)((key0 + row) * KROW + ch * 16);
-      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
-      vst[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (uint32_t)((key0 + row) * KROW + ch * 16), 0, 0);
     }
   };
-
-  auto store_tile = [&](int stage) {
-    uint8_t* ks = smem + stage * STAGE;
-    uint8_t* vs = ks + KSTAGE;
+  auto load_v = [&](int key0) {
 #pragma unroll
     for (int it = 0; it < CH_T; ++it) {
       const int e = tid + it * T;
       const int row = e / (D / 8), ch = e % (D / 8);
-      *(u32x4*)(ks + row * KP + ch * 16) = kst[it];
-      *(u32x4*)(vs + row * VP + ch * 16) = vst[it];
+      vst[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, (uint32_t)((key0 + row) * KROW + ch * 16), 0, 0);
+    }
+  };
+  auto store_k = [&](int stage) {
+#pragma unroll
+    for (int it = 0; it < CH_T; ++it) {
+      const int e = tid + it * T;
+      const int row = e / (D / 8), ch = e % (D / 8);
+      *(u32x4*)(kring + stage * KSTAGE + row * KP + ch * 16) = kst[it];
+    }
+  };
+  auto store_v = [&](int stage) {
+#pragma unroll
+    for (int it = 0; it < CH_T; ++it) {
+      const int e = tid + it * T;
+      const int row = e / (D / 8), ch = e % (D / 8);
+      *(u32x4*)(vring + stage * VSTAGE + row * VP + ch * 16) = vst[it];
     }
   };
 
@@ -257,7 +280,7 @@ void fa2_fwd_kernel(Args a) {
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
   const float c = a.c;
-  const bool c_nonneg = c >= 0.f;
+  const bool c_neg = c < 0.f;
   const int kbase = lr * KP + lh * 16;   // this lane's K fragment: row 32*kb + lr, chunk 2*dk + lh
   // V^T fragments come from row-major V through the LDS transpose read.  In
   // each 16-lane group g, lane (4e + c) fetches 4 elements of key row
@@ -267,12 +290,8 @@ void fa2_fwd_kernel(Args a) {
   const int vg = lane >> 4;
   const int vbase = (4 * (vg >> 1) + ((lane >> 2) & 3)) * VP + 32 * (vg & 1) + 8 * (lane & 3);
 
-  auto compute = [&](int stage, int key0, bool masked) {
-    const uint8_t* ks = smem + stage * STAGE;
-    const uint8_t* vs = ks + KSTAGE;
-
-    // S^T = K Q^T for every (key block, query block)
-    f32x16 s[QB][KB];
+  // S^T = K Q^T for every (key block, query block), K from one LDS stage
+  auto scores = [&](const uint8_t* ks, f32x16 (&s)[QB][KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -286,18 +305,21 @@ void fa2_fwd_kernel(Args a) {
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = E::mfma(kf, qf[qb][dk], s[qb][kb]);
       }
     }
+  };
 
-    // online softmax, one query per lane and query block
-    u32x4 pf[QB][KB][2];
+  // online softmax of one tile of scores: updates m, l, returns P and alpha
+  auto softmax = [&](f32x16 (&s)[QB][KB], int key0, bool masked, u32x4 (&pf)[QB][KB][2],
+                     float (&alpha)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float cc = c;
       float m_tile;
       if (masked) {
-        // tiles that cross the diagonal or the end of the sequence: scale
-        // first, then masked scores are -inf and exp2 gives exactly 0
+        // tiles that cross the diagonal or the end of the sequence (and every
+        // tile when scale < 0): scale first, masked scores become -inf and
+        // exp2 gives exactly 0 for them
         const int q = q_w + qb * 32 + lr;
-        float e = -INFINITY;
+        float e0 = -INFINITY, e1 = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -306,33 +328,38 @@ void fa2_fwd_kernel(Args a) {
             const bool vis = key < N && (!CAUSAL || key <= q);
             const float t = vis ? s[qb][kb][r] * c : -INFINITY;
             s[qb][kb][r] = t;
-            e = fmaxf(e, t);
+            if (r & 1) e1 = fmaxf(e1, t); else e0 = fmaxf(e0, t);
           }
-        m_tile = max_halves(e);
+        m_tile = max_halves(fmaxf(e0, e1));
         cc = 1.f;
-      } else if (c_nonneg) {
-        // max of c*s is c*max(s) for c >= 0 ...
-        float e = s[qb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) e = fmaxf(e, s[qb][kb][r]);
-        m_tile = max_halves(e) * c;
       } else {
-        // ... and c*min(s) for c < 0
-        float e = s[qb][0][0];
+        // c >= 0 here, so the tile max of c*s is c*max(s); two chains
+        float e0 = s[qb][0][0], e1 = s[qb][0][1];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e = fminf(e, s[qb][kb][r]);
-        m_tile = min_halves(e) * c;
+          for (int r = 0; r < 16; r += 4) {
+            e0 = fmaxf(e0, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+            e1 = fmaxf(e1, fmaxf(s[qb][kb][r + 2], s[qb][kb][r + 3]));
+          }
+        m_tile = max_halves(fmaxf(e0, e1)) * c;
       }
-      const float m_new = fmaxf(m_run[qb], m_tile);
+      // Lazy reference: the row's reference max moves only when the tile max
+      // exceeds it by more than kLazyRescale (or it is still -inf); otherwise
+      // alpha = 1 and p = 2^(s*c - m) stays below 2^kLazyRescale.  O = acc / l
+      // and LSE = m + log2 l use the same reference, so the result is the same
+      // exact value (the conditional rescale of the v4 diagram, exact form).
+      const float m_old = m_run[qb];
+      const float m_new = (m_tile > m_old + kLazyRescale) ? m_tile : m_old;
       // a row with no visible key so far keeps m = -inf; never form -inf - -inf
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
+      alpha[qb] = __builtin_amdgcn_exp2f(m_old - m_use);
       m_run[qb] = m_new;
-      float rs = 0.f;
+      // p = 2^(s*c - m): one FMA + one exp2 per score.  The row sum is taken
+      // over the fp32 p (two chains): summing the 16-bit P instead would put
+      // its rounding (2^-9 relative in bf16) straight into LSE.  P is rounded
+      // to the input type for the P.V product.
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -341,18 +368,28 @@ void fa2_fwd_kernel(Args a) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * st + t], cc, -m_use));
-            rs += p[t];
+            if (t & 1) rs1 += p[t]; else rs0 += p[t];
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) pf[qb][kb][st][t] = E::pack(p[2 * t], p[2 * t + 1]);
         }
       }
-      l_run[qb] = l_run[qb] * alpha + rs;
-      // rescale acc; exact skip when no row of the wave changed its max
-      if (__any(alpha != 1.f)) {
+      l_run[qb] = l_run[qb] * alpha[qb] + (rs0 + rs1);
+    }
+  };
+
+  // acc = alpha * acc (only when some row moved its reference), then
+  // O^T += V^T P^T with V from one LDS stage
+  auto rescale_pv = [&](const uint8_t* vs, const u32x4 (&pf)[QB][KB][2], const float (&alpha)[QB]) {
+    // rescale acc only when some row of the wave moved its reference
+    bool moved = false;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-      }
+    for (int qb = 0; qb < QB; ++qb) moved |= alpha[qb] != 1.f;
+    if (__any(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha[qb];
     }
 
     // O^T += V^T P^T
@@ -373,23 +410,195 @@ void fa2_fwd_kernel(Args a) {
     }
   };
 
-  // ---- main loop: 2-stage LDS ring, next tile's loads overlap compute ----
-  load_tile(0);
-  store_tile(0);
-  // Every load issued so far (Q fragments, first tile) is complete here.
-  // Saying so explicitly keeps the compiler from placing waits for the Q
-  // loads inside the loop, where they would also wait for the prefetch of
-  // the next tile and expose its latency on every iteration.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const int key0 = j * BC;
-    if (j + 1 < nt) load_tile(key0 + BC);
-    const bool skip = CAUSAL && key0 > q_w + 32 * QB - 1;       // tile entirely above the diagonal
-    const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
-    if (!skip) compute(j & 1, key0, masked);
-    if (j + 1 < nt) store_tile((j + 1) & 1);
+  auto tile_skip = [&](int key0) {     // tile entirely above this wave's diagonal
+    return CAUSAL && key0 > q_w + 32 * QB - 1;
+  };
+  auto tile_masked = [&](int key0) {   // tile crosses the diagonal or the end of the sequence
+    return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w) || c_neg;
+  };
+
+  if constexpr (TL::PIPE == 0) {
+    // ---- main loop: 2-stage LDS ring, next tile's loads overlap compute ----
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    // Every load issued so far (Q fragments, first tile) is complete here.
+    // Saying so explicitly keeps the compiler from placing waits for the Q
+    // loads inside the loop, where they would also wait for the prefetch of
+    // the next tile and expose its latency on every iteration.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    for (int j = 0; j < nt; ++j) {
+      const int key0 = j * BC;
+      if (j + 1 < nt) {
+        load_k(key0 + BC);
+        load_v(key0 + BC);
+      }
+      if (!tile_skip(key0)) {
+        f32x16 sc[QB][KB];
+        u32x4 pf[QB][KB][2];
+        float alpha[QB];
+        scores(kring + (j & 1) * KSTAGE, sc);
+        softmax(sc, key0, tile_masked(key0), pf, alpha);
+        rescale_pv(vring + (j & 1) * VSTAGE, pf, alpha);
+      }
+      if (j + 1 < nt) {
+        store_k((j + 1) & 1);
+        store_v((j + 1) & 1);
+      }
+      __syncthreads();
+    }
+  } else if constexpr (TL::PIPE == 3) {
+    // ---- ping-pong schedule -------------------------------------------------
+    // The NW waves form two groups of NW/2; wave i runs on SIMD i % 4, so with
+    // NW = 8 each SIMD holds one wave of each group.  Time is cut into
+    // half-steps separated by barriers.  In half-step h a group whose phase
+    // h - g is even runs its MFMA phase for tile t = (h - g) / 2 (P.V of tile
+    // t-1, then the scores of tile t); a group whose phase is odd runs its
+    // softmax phase for tile (h - g - 1) / 2.  The two groups are always in
+    // opposite phases, so on every SIMD one wave feeds the MFMA pipe while the
+    // other keeps the VALU busy.
+    //   K_t lives in K stage t&1, V_t in V stage t&1.  Group 1 writes K_{t+2}
+    //   in its softmax phase of tile t (half-step 2t+2; K_t was last read in
+    //   half-step 2t+1) and then fetches K_{t+3}; group 0 writes V_t in its
+    //   softmax phase of tile t (half-step 2t+1; V_{t-2} was last read in
+    //   half-step 2t-1) and fetches V_{t+1}.  Every global load thus has two
+    //   half-steps to land.
+    static_assert(NW % 2 == 0, "ping-pong needs an even number of waves");
+    constexpr int TG = T / 2;          // threads per group
+    constexpr int CHG = CH / TG;       // 16-byte chunks per thread and tile
+    static_assert(CH % TG == 0, "tile copy must split evenly over a group");
+    const int grp = wave / (NW / 2);
+    const int gtid = tid - grp * TG;
+    u32x4 gst[CHG];
+    const __amdgpu_buffer_rsrc_t grs = grp ? kr : vr;
+    auto gload = [&](int key0) {
+#pragma unroll
+      for (int it = 0; it < CHG; ++it) {
+        const int e = gtid + it * TG;
+        const int row = e / (D / 8), ch = e % (D / 8);
+        gst[it] = __builtin_amdgcn_raw_buffer_load_b128(grs, (uint32_t)((key0 + row) * KROW + ch * 16), 0, 0);
+      }
+    };
+    auto gstore = [&](int stage) {
+      uint8_t* base = grp ? kring + stage * KSTAGE : vring + stage * VSTAGE;
+      const int pitch = grp ? KP : VP;
+#pragma unroll
+      for (int it = 0; it < CHG; ++it) {
+        const int e = gtid + it * TG;
+        const int row = e / (D / 8), ch = e % (D / 8);
+        *(u32x4*)(base + row * pitch + ch * 16) = gst[it];
+      }
+    };
+    // prologue: K_0, K_1 into LDS; group 0 holds V_0, group 1 holds K_2
+    load_k(0);
+    store_k(0);
+    if (nt > 1) {
+      load_k(BC);
+      store_k(1);
+    }
+    if (grp == 0) gload(0);
+    else if (nt > 2) gload(2 * BC);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    f32x16 sc[QB][KB];
+    u32x4 pf[QB][KB][2];
+    float alpha[QB];
+    for (int h = 0; h < 2 * nt + 2; ++h) {
+      const int ph = h - grp;
+      if (ph >= 0 && (ph & 1) == 0) {
+        const int t = ph >> 1;
+        __builtin_amdgcn_s_setprio(1);
+        if (t >= 1 && !tile_skip((t - 1) * BC)) rescale_pv(vring + ((t - 1) & 1) * VSTAGE, pf, alpha);
+        if (t < nt && !tile_skip(t * BC)) scores(kring + (t & 1) * KSTAGE, sc);
+        __builtin_amdgcn_s_setprio(0);
+      } else if (ph >= 1) {
+        const int t = (ph - 1) >> 1;
+        if (t < nt) {
+          if (!tile_skip(t * BC)) softmax(sc, t * BC, tile_masked(t * BC), pf, alpha);
+          if (grp == 0) {
+            gstore(t & 1);                         // V_t
+            if (t + 1 < nt) gload((t + 1) * BC);   // V_{t+1}
+          } else {
+            if (t + 2 < nt) gstore(t & 1);         // K_{t+2}
+            if (t + 3 < nt) gload((t + 3) * BC);   // K_{t+3}
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // ---- software-pipelined loop ------------------------------------------
+    // Iteration j: scores of tile j+1 (K_{j+1} from K stage (j+1)&1) are
+    // issued together with the softmax of tile j, then acc += V_j P_j (V
+    // stage j&1).  K_{j+2} and V_{j+1} are fetched during the iteration and
+    // written to K stage j&1 and V stage (j+1)&1, which nobody reads in
+    // iteration j; one barrier per iteration publishes them.
+    const int nclean = c_neg ? 0 : (CAUSAL ? min(q_wg, N) / BC : N / BC);  // tiles no wave masks
+    const int nfast = min(nclean, nt - 1);
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (nt > 1) {
+      load_k(BC);
+      store_k(1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    f32x16 sc[QB][KB];
+    if (!tile_skip(0)) scores(kring, sc);
+
+    auto iteration = [&](int j, auto has_next_tag, auto fast_tag) {
+      constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+      constexpr bool FAST = decltype(fast_tag)::value;
+      const int key0 = j * BC;
+      const bool load2 = HAS_NEXT && j + 2 < nt;
+      if (load2) load_k(key0 + 2 * BC);
+      if (HAS_NEXT) load_v(key0 + BC);
+      f32x16 sn[QB][KB];
+      u32x4 pf[QB][KB][2];
+      float alpha[QB];
+      if constexpr (FAST) {
+        // no mask, no skip: one basic block for the MFMAs and the softmax
+        scores(kring + ((j + 1) & 1) * KSTAGE, sn);
+        softmax(sc, key0, false, pf, alpha);
+        if constexpr (TL::PIPE == 2) {
+          // issue order: the tile loads, then (LDS read, MFMA, VALU x n) per
+          // score MFMA, so the softmax VALU work fills the MFMA shadow
+#pragma unroll
+          for (int i = 0; i < 2 * CH_T; ++i) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+#pragma unroll
+          for (int i = 0; i < QB * KB * DK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+          }
+        }
+        rescale_pv(vring + (j & 1) * VSTAGE, pf, alpha);
+      } else {
+        if (HAS_NEXT && !tile_skip(key0 + BC)) scores(kring + ((j + 1) & 1) * KSTAGE, sn);
+        if (!tile_skip(key0)) {
+          softmax(sc, key0, tile_masked(key0), pf, alpha);
+          rescale_pv(vring + (j & 1) * VSTAGE, pf, alpha);
+        }
+      }
+      if (load2) store_k(j & 1);
+      if (HAS_NEXT) store_v((j + 1) & 1);
+      __syncthreads();
+      if constexpr (HAS_NEXT) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sc[qb][kb] = sn[qb][kb];
+      }
+    };
+    int j = 0;
+    for (; j < nfast; ++j) iteration(j, std::true_type{}, std::true_type{});
+    for (; j < nt - 1; ++j) iteration(j, std::true_type{}, std::false_type{});
+    iteration(nt - 1, std::false_type{}, std::false_type{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ---------------------

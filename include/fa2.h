@@ -26,7 +26,7 @@
  * Arithmetic.  Both products run on the MFMA units with 16-bit inputs and
  * fp32 accumulation; the softmax runs in fp32.  P is rounded to the input
  * dtype (round-to-nearest-even) before the P.V product; the row sum is taken
- * from the fp32 P.  O is written rounded to nearest even in the input dtype.
+ * over the fp32 P.  O is written rounded to nearest even in the input dtype.
  *
  * Ownership and execution.  All tensor pointers are DEVICE pointers owned by
  * the caller.  The library allocates no memory, frees nothing, keeps no
