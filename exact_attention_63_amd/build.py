@@ -30,6 +30,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # no packed fp32 arithmetic (v_pk_*_f32) in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code only: no NaN-quieting canonicalisation around max/min, so a
+    # 3-input max is one v_max3_f32 (infinities, used for masking, are kept)
+    "-Xarch_device", "-fno-honor-nans",
     "-Rpass-analysis=kernel-resource-usage",
 ]
 

@@ -113,6 +113,33 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
 }
 
+// XOR swizzle of the 16-byte chunks of an unpadded LDS row of D 16-bit
+// elements (D = 128: 16 chunks, D = 64: 8 chunks).  With it, the 16 rows read
+// at one chunk by a 16-byte fragment read, and the 4 rows x 64 bytes of one
+// transpose read, fall on distinct banks of the 64 x 4-byte bank array.
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    static_assert(D == 64, "d must be 64 or 128");
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l of the wave writes
+// lds + 16*l (buffer_load_dwordx4 ... lds; out-of-range lanes write zeros).
+// Kept in a device-only function: used directly in the kernel body, the
+// builtin makes the host compilation pass drop the kernel's launch stub.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset,
+                                          int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, voffset,
+                                           soffset, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (n < 16) with expcnt and lgkmcnt left at their maxima.
+#define FA2_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
 // ds_read_b64_tr_b16: transpose read of 16-bit elements (see the V fragment
 // comment in the kernel for the lane mapping).
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
@@ -144,7 +171,9 @@ struct Tile {
   // current tile's softmax (K staged two tiles ahead, V one tile ahead);
   // PIPE 2: additionally ask the scheduler to interleave those MFMAs with the
   // softmax VALU work one by one, so that one wave keeps both pipes busy;
-  // PIPE 3: ping-pong between two wave groups in opposite phases.
+  // PIPE 3: ping-pong between two wave groups in opposite phases;
+  // PIPE 4 / 5: K and V copied straight from HBM into a 3- / 2-stage LDS ring
+  // (buffer_load ... lds), swizzled unpadded rows.
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -169,9 +198,15 @@ void fa2_fwd_kernel(Args a) {
   constexpr int CH = BC * D / 8;        // 16-byte chunks per K (or V) tile
   constexpr int CH_T = CH / T;          // ... per thread
   static_assert(CH % T == 0, "tile copy must split evenly over threads");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+  // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
+  // [key][d] K and V tiles
+  constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
+  constexpr int NS = TL::PIPE == 4 ? 3 : 2;       // LDS stages of the direct-copy loops
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5;
+  constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -449,6 +484,125 @@ void fa2_fwd_kernel(Args a) {
       }
       __syncthreads();
     }
+  } else if constexpr (DMA) {
+    // ---- direct global->LDS copies, NS-stage ring ---------------------------
+    // Each K/V tile is fetched NS-1 tiles ahead with buffer_load ... lds: the
+    // data never passes through VGPRs, and every wave only waits for its own
+    // copies of the tile it is about to use.  One DMA instruction writes 1 KiB
+    // of LDS, lane l at byte 16*l, so the bank-conflict fix is an XOR swizzle
+    // of 16-byte chunks inside each row (chunk_swizzle) applied through the
+    // choice of source address; the fragment reads apply the same swizzle.
+    // LDS: K stage s at s*TSZ, V stage s at (NS + s)*TSZ.  The loop is
+    // unrolled by the NS stages so that every LDS offset is an immediate on a
+    // handful of per-lane base registers.
+    constexpr int NI = TSZ / 1024;     // DMA instructions per tile and tensor
+    static_assert(NI % NW == 0, "tile DMA must split evenly over the waves");
+    constexpr int NIW = NI / NW;       // ... per wave
+    // per-lane source offsets of this wave's DMA instructions (row, logical chunk)
+    uint32_t dsrc[NIW];
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const int b = (wave * NIW + k) * 1024 + 16 * lane;
+      const int row = b / KROW, phys = (b % KROW) / 16;
+      dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+    }
+    auto dma = [&](int tile, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int base = tile * BC * KROW;      // uniform: the SGPR offset of the copy
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const int dst = (wave * NIW + k) * 1024;
+        lds_dma16(kr, smem + S * TSZ + dst, dsrc[k], base);
+        lds_dma16(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
+      }
+    };
+    // fragment addresses (see chunk_swizzle): K row 32*kb + lr, chunk 2*dk + lh;
+    // V rows 32*kb + 16*st + 8*x + 4*(g/2) + e, chunk 4*db + 2*(g%2) + c/2
+    const int kfb = lr * KROW + 16 * (lh ^ chunk_swizzle<D>(lr));
+    const int vgq = lane >> 4, ve = (lane >> 2) & 3, vc = lane & 3;
+    const int vfb = (4 * (vgq >> 1) + ve) * KROW + 8 * (vc & 1) +
+                    (D == 128 ? 64 * ve : 64 * (ve >> 1)) +
+                    16 * ((2 * (vgq & 1) | (vc >> 1)) ^ (vgq >> 1));
+    int ka[DK];                 // K fragment base of each 16-wide d step
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) ka[dk] = kfb ^ (32 * dk);
+    int va[DB][2];              // V fragment base of each 32-wide d block, low/high 8 keys
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      va[db][0] = NS * TSZ + (vfb ^ (64 * db));
+      va[db][1] = NS * TSZ + 8 * KROW + (vfb ^ (64 * db) ^ 32);
+    }
+    auto compute_sw = [&](int key0, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      f32x16 sv[QB][KB];
+      u32x4 pfv[QB][KB][2];
+      float al[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sv[qb][kb] = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 kf = *(const u32x4*)(smem + ka[dk] + (S * TSZ + 32 * kb * KROW));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sv[qb][kb] = E::mfma(kf, qf[qb][dk], sv[qb][kb]);
+        }
+      }
+      softmax(sv, key0, tile_masked(key0), pfv, al);
+      bool moved = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) moved |= al[qb] != 1.f;
+      if (__any(moved)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[qb][db] *= al[qb];
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int roff = S * TSZ + (32 * kb + 16 * st) * KROW;
+            const u32x2 lo = lds_read_tr16(smem + va[db][0] + roff);   // keys 4h + 0..3 of the step
+            const u32x2 hi = lds_read_tr16(smem + va[db][1] + roff);   // keys 8 + 4h + 0..3
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mfma(vf, pfv[qb][kb][st], acc[qb][db]);
+          }
+        }
+      }
+    };
+    auto step = [&](int j, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;   // == j % NS
+      // this wave's copies of tile j are done once at most the copies of the
+      // tiles issued after it (NS-2 of them, 2*NIW instructions each) remain
+      if constexpr (NS == 3) {
+        if (j + 1 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+      } else {
+        FA2_WAIT_VMCNT(0);
+      }
+      // every wave's tile j has landed and every wave has finished tile j-1,
+      // so stage (j-1)%NS == (j+NS-1)%NS may be refilled
+      __syncthreads();
+      if (j + NS - 1 < nt) dma(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+      if (!tile_skip(j * BC)) compute_sw(j * BC, stage_tag);
+    };
+    dma(0, std::integral_constant<int, 0>{});
+    if (NS == 3 && nt > 1) dma(1, std::integral_constant<int, 1 % NS>{});
+    // Q fragments were loaded before the copies: wait for them only
+    if (NS == 3 && nt > 1) FA2_WAIT_VMCNT(4 * NIW); else FA2_WAIT_VMCNT(2 * NIW);
+    int j = 0;
+    for (; j + NS <= nt; j += NS) {
+      step(j, std::integral_constant<int, 0>{});
+      step(j + 1, std::integral_constant<int, 1>{});
+      if constexpr (NS == 3) step(j + 2, std::integral_constant<int, 2 % NS>{});
+    }
+    if (j < nt) step(j, std::integral_constant<int, 0>{});
+    if (NS == 3 && j + 1 < nt) step(j + 1, std::integral_constant<int, 1>{});
   } else if constexpr (TL::PIPE == 3) {
     // ---- ping-pong schedule -------------------------------------------------
     // The NW waves form two groups of NW/2; wave i runs on SIMD i % 4, so with
