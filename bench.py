@@ -27,28 +27,33 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS (and % of MFMA peak) at N=2048,d=128 bf16"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}   # MI355X dense MFMA peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_63_amd", "csrc", f)
-                  for f in ("fa2_fwd_kernel.hpp", "fa2_api.hip")]
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_fwd_kernel.hpp")
 
 
-def kernel_source_hash() -> str:
+def kernel_identity(w, variant: int = 0) -> str:
+    """Hash of the kernel template source and the tile configuration that the
+    workload runs with: the counters recorded for one identity are only reused
+    for exactly that kernel."""
+    import exact_attention_63_amd as fa2
+    vi = variant or fa2.default_variant(0 if w.dtype == "fp16" else 1, w.d, w.causal)
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    with open(KERNEL_SOURCE, "rb") as f:
+        h.update(f.read())
+    h.update(fa2.variant_name(vi).encode())
+    h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(w, variant: int = 0):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    the kernel sources changed since the counters were taken."""
+    the kernel changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(workload)
-    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+    ent = rec.get(w.name)
+    if not ent or ent.get("kernel_identity") != kernel_identity(w, variant):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -71,31 +76,31 @@ def time_gpu(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps, wall / steps * 1e3
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The fp64 CPU oracle timed on whole heads of the same workload until about
-    budget_s seconds of work are done (at least one head)."""
-    import numpy as np
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The fp64 CPU oracle timed on whole heads of the same workload (in order)
+    until about budget_s seconds of work are done or every head is done."""
     import oracle
-    from workloads import make_inputs, to_f64
+    from workloads import workload_inputs, to_f64
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    q, k, v = make_inputs(1, 8, w.N, w.d, w.dtype, w.seed, w.sigma, w.key_offset)
-    q64, k64, v64 = to_f64(q)[0], to_f64(k)[0], to_f64(v)[0]
+    q, k, v = workload_inputs(w)
+    nh = w.B * w.H
     heads = 0
     t0 = time.perf_counter()
-    while heads < 8:
-        oracle.attention_3pass(q64[heads], k64[heads], v64[heads], w.causal, w.scale)
+    while heads < nh:
+        b, h = divmod(heads, w.H)
+        oracle.attention_3pass(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.causal, w.scale)
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    flops_per_head = w.flops / (w.B * w.H)
+    flops_per_head = w.flops / nh
     return {"value": round(heads * flops_per_head / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
             "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads (all {w.N} rows each) of {w.name}, fp64 NumPy "
+            "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, fp64 NumPy "
                       f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
@@ -129,8 +134,8 @@ def copy_calibration(nbytes: int, steps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", type=int, default=0, help="tile variant (0 = tuned default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,7 +162,7 @@ def main():
     ms, wall_ms = run_workload(w, args.steps, args.warmup, args.variant)
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(w, args.variant)
 
     if args.all:
         print(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}", file=sys.stderr)

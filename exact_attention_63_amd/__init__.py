@@ -17,6 +17,7 @@ import os
 
 __all__ = [
     "forward", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "default_variant",
     "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
     "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
     "Fa2Error",
@@ -48,6 +49,7 @@ EXPORTS = {
     "fa2_fwd": (_I, _FWD12 + [_I]),
     "fa2_fwd_variant": (_I, _FWD12 + [_I, _I]),
     "fa2_fwd_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+    "fa2_default_variant": (_I, [_I, _I, _I]),
     "fa2_num_variants": (_I, []),
     "fa2_variant_name": (ctypes.c_char_p, [_I]),
     "fa2_status_string": (ctypes.c_char_p, [_I]),
@@ -95,6 +97,15 @@ def num_variants() -> int:
 def variant_name(variant: int) -> str | None:
     s = lib().fa2_variant_name(variant)
     return None if s is None else s.decode()
+
+
+def default_variant(dtype, d: int, causal: bool) -> int:
+    """The tile variant that variant 0 resolves to (dtype: torch dtype or FA2_DTYPE_*)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    rc = lib().fa2_default_variant(code, d, int(bool(causal)))
+    if rc < 0:
+        raise Fa2Error(rc, "fa2_default_variant")
+    return rc
 
 
 def version() -> int:

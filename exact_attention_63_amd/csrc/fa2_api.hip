@@ -53,6 +53,10 @@ const Variant kVariants[] = {
     make_variant<Tile<8, 1, 2, 2, 3>>("w8_q32_k64_pingpong"),     // two 4-wave groups in opposite phases
     make_variant<Tile<8, 1, 2, 2, 4>>("w8_q32_k64_dma3"),         // direct global->LDS copies, 3 stages
     make_variant<Tile<4, 1, 2, 2, 5>>("w4_q32_k64_dma2"),         // 4 waves, 2 stages: two workgroups per CU
+    make_variant<Tile<8, 1, 2, 2, 4, 4>>("w8_q32_k64_dma3_look4"), // dma3 + 4 operand reads ahead
+    make_variant<Tile<8, 1, 2, 2, 4, 6>>("w8_q32_k64_dma3_look6"), // dma3 + 6 operand reads ahead
+    make_variant<Tile<8, 1, 4, 2, 5>>("w8_q32_k128_dma2"),        // 128-key tiles, 2-stage ring
+    make_variant<Tile<8, 1, 4, 2, 5, 4>>("w8_q32_k128_dma2_look4"), // ... with 4 operand reads ahead
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -172,6 +176,13 @@ FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const 
                              float scale, int dtype, int variant) {
   const int st = check(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, variant);
   return st == kEmpty ? FA2_OK : st;
+}
+
+FA2_EXPORT int fa2_default_variant(int dtype, int d, int causal) {
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_ARG;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  return default_variant(dtype == FA2_DTYPE_BF16, d, causal);
 }
 
 FA2_EXPORT int fa2_num_variants(void) { return kNumVariants; }

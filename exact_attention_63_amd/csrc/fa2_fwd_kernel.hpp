@@ -164,16 +164,20 @@ struct Args {
 //   NW : waves per workgroup         QB : 32-query blocks per wave
 //   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
 //   PIPE: software-pipelined main loop (see below)
-template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0>
+template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0, int LOOK_ = 0>
 struct Tile {
   static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  // LOOK (direct-copy loops): keep this many score-MFMA operand reads in
+  // flight ahead of the MFMAs (0: leave the order to the compiler)
+  static constexpr int LOOK = LOOK_;
   // PIPE 1: issue the next tile's score MFMAs in the same basic block as the
   // current tile's softmax (K staged two tiles ahead, V one tile ahead);
   // PIPE 2: additionally ask the scheduler to interleave those MFMAs with the
   // softmax VALU work one by one, so that one wave keeps both pipes busy;
   // PIPE 3: ping-pong between two wave groups in opposite phases;
   // PIPE 4 / 5: K and V copied straight from HBM into a 3- / 2-stage LDS ring
-  // (buffer_load ... lds), swizzled unpadded rows.
+  // (buffer_load ... lds), swizzled unpadded rows;
+  // PIPE 6: 4-stage ring with the pipelined, interleaved loop of PIPE 2.
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -201,8 +205,9 @@ void fa2_fwd_kernel(Args a) {
   // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
   // [key][d] K and V tiles
   constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
-  constexpr int NS = TL::PIPE == 4 ? 3 : 2;       // LDS stages of the direct-copy loops
-  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5;
+  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 6: 4)
+  constexpr int NS = TL::PIPE == 4 ? 3 : (TL::PIPE == 6 ? 4 : 2);
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 6;
   constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 
@@ -532,11 +537,9 @@ void fa2_fwd_kernel(Args a) {
       va[db][0] = NS * TSZ + (vfb ^ (64 * db));
       va[db][1] = NS * TSZ + 8 * KROW + (vfb ^ (64 * db) ^ 32);
     }
-    auto compute_sw = [&](int key0, auto stage_tag) {
+    // S^T = K Q^T from K stage S
+    auto scores_st = [&](f32x16 (&sv)[QB][KB], auto stage_tag) {
       constexpr int S = decltype(stage_tag)::value;
-      f32x16 sv[QB][KB];
-      u32x4 pfv[QB][KB][2];
-      float al[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -550,7 +553,26 @@ void fa2_fwd_kernel(Args a) {
           for (int qb = 0; qb < QB; ++qb) sv[qb][kb] = E::mfma(kf, qf[qb][dk], sv[qb][kb]);
         }
       }
-      softmax(sv, key0, tile_masked(key0), pfv, al);
+    };
+    // issue order for a score product: LOOK fragment reads ahead, then one
+    // MFMA per further read, with VALU instructions of the same basic block
+    // (VPM per MFMA) filling the MFMA shadow
+    auto order_scores = [&](auto look_tag, auto vpm_tag) {
+      constexpr int LOOK = decltype(look_tag)::value, VPM = decltype(vpm_tag)::value;
+      constexpr int NM = QB * KB * DK, NR = KB * DK;
+      static_assert(QB == 1, "read lookahead assumes one fragment per MFMA");
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < NR - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        if constexpr (VPM > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
+      }
+    };
+    // acc = alpha * acc when some row moved its reference, then O^T += V^T P^T
+    // from V stage S
+    auto pv_st = [&](const u32x4 (&pfv)[QB][KB][2], const float (&al)[QB], auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
       bool moved = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) moved |= al[qb] != 1.f;
@@ -575,34 +597,113 @@ void fa2_fwd_kernel(Args a) {
           }
         }
       }
-    };
-    auto step = [&](int j, auto stage_tag) {
-      constexpr int S = decltype(stage_tag)::value;   // == j % NS
-      // this wave's copies of tile j are done once at most the copies of the
-      // tiles issued after it (NS-2 of them, 2*NIW instructions each) remain
-      if constexpr (NS == 3) {
-        if (j + 1 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
-      } else {
-        FA2_WAIT_VMCNT(0);
+      if constexpr (TL::LOOK > 0) {
+        // two transpose reads per MFMA, 2*LOOK reads ahead
+        constexpr int NM = DB * KB * 2;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * TL::LOOK, 0);
+#pragma unroll
+        for (int i = 0; i < NM - TL::LOOK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, TL::LOOK, 0);
       }
-      // every wave's tile j has landed and every wave has finished tile j-1,
-      // so stage (j-1)%NS == (j+NS-1)%NS may be refilled
-      __syncthreads();
-      if (j + NS - 1 < nt) dma(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
-      if (!tile_skip(j * BC)) compute_sw(j * BC, stage_tag);
     };
-    dma(0, std::integral_constant<int, 0>{});
-    if (NS == 3 && nt > 1) dma(1, std::integral_constant<int, 1 % NS>{});
-    // Q fragments were loaded before the copies: wait for them only
-    if (NS == 3 && nt > 1) FA2_WAIT_VMCNT(4 * NIW); else FA2_WAIT_VMCNT(2 * NIW);
-    int j = 0;
-    for (; j + NS <= nt; j += NS) {
-      step(j, std::integral_constant<int, 0>{});
-      step(j + 1, std::integral_constant<int, 1>{});
-      if constexpr (NS == 3) step(j + 2, std::integral_constant<int, 2 % NS>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    if constexpr (TL::PIPE != 6) {
+      auto step = [&](int j, auto stage_tag) {
+        constexpr int S = decltype(stage_tag)::value;   // == j % NS
+        // this wave's copies of tile j are done once at most the copies of the
+        // tiles issued after it (NS-2 of them, 2*NIW instructions each) remain
+        if constexpr (NS == 3) {
+          if (j + 1 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+        } else {
+          FA2_WAIT_VMCNT(0);
+        }
+        // every wave's tile j has landed and every wave has finished tile j-1,
+        // so stage (j-1)%NS == (j+NS-1)%NS may be refilled
+        __syncthreads();
+        if (j + NS - 1 < nt) dma(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+        const int key0 = j * BC;
+        if (!tile_skip(key0)) {
+          f32x16 sv[QB][KB];
+          u32x4 pfv[QB][KB][2];
+          float al[QB];
+          scores_st(sv, stage_tag);
+          if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
+          softmax(sv, key0, tile_masked(key0), pfv, al);
+          pv_st(pfv, al, stage_tag);
+        }
+      };
+      dma(0, I0{});
+      if (NS == 3 && nt > 1) dma(1, std::integral_constant<int, 1 % NS>{});
+      // Q fragments were loaded before the copies: wait for them only
+      if (NS == 3 && nt > 1) FA2_WAIT_VMCNT(4 * NIW); else FA2_WAIT_VMCNT(2 * NIW);
+      int j = 0;
+      for (; j + NS <= nt; j += NS) {
+        step(j, I0{});
+        step(j + 1, I1{});
+        if constexpr (NS == 3) step(j + 2, std::integral_constant<int, 2 % NS>{});
+      }
+      if (j < nt) step(j, I0{});
+      if (NS == 3 && j + 1 < nt) step(j + 1, I1{});
+    } else {
+      // Software-pipelined over a 4-stage ring: step j waits for tile j+1,
+      // refills stage (j+3)%4 (tile j-1's, finished by everyone at the
+      // barrier), then issues the score MFMAs of tile j+1 one by one between
+      // the softmax instructions of tile j, and finally P.V of tile j.
+      static_assert(NS == 4, "pipelined direct-copy loop uses 4 stages");
+      const int nclean = c_neg ? 0 : (CAUSAL ? min(q_wg, N) / BC : N / BC);   // tiles no wave masks
+      f32x16 sa[QB][KB], sb[QB][KB];   // scores of tiles j and j+1, roles alternate
+      auto pstep = [&](int j, auto stage_tag, f32x16 (&sc)[QB][KB], f32x16 (&sn)[QB][KB]) {
+        constexpr int S = decltype(stage_tag)::value;   // == j % 4
+        using SN = std::integral_constant<int, (S + 1) % 4>;
+        const bool next = j + 1 < nt;
+        // tile j+1 must have landed; tile j+2 may still be in flight
+        if (j + 2 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+        __syncthreads();
+        if (j + 3 < nt) dma(j + 3, std::integral_constant<int, (S + 3) % 4>{});
+        const int key0 = j * BC;
+        u32x4 pfv[QB][KB][2];
+        float al[QB];
+        if (next && j < nclean) {
+          // steady state: tile j unmasked for every wave, tile j+1 needed by
+          // every wave; one basic block for the MFMAs and the softmax
+          scores_st(sn, SN{});
+          softmax(sc, key0, false, pfv, al);
+          order_scores(std::integral_constant<int, (TL::LOOK > 0 ? TL::LOOK : 4)>{},
+                       std::integral_constant<int, 0>{});
+          pv_st(pfv, al, stage_tag);
+        } else {
+          if (next && !tile_skip(key0 + BC)) scores_st(sn, SN{});
+          if (!tile_skip(key0)) {
+            softmax(sc, key0, tile_masked(key0), pfv, al);
+            pv_st(pfv, al, stage_tag);
+          }
+        }
+      };
+      dma(0, I0{});
+      if (nt > 1) dma(1, I1{});
+      if (nt > 2) dma(2, I2{});
+      // Q done (older than the copies); tile 0 landed: at most tiles 1, 2 in flight
+      if (nt > 2) FA2_WAIT_VMCNT(4 * NIW); else if (nt > 1) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+      __syncthreads();
+      if (!tile_skip(0)) scores_st(sa, I0{});
+      int j = 0;
+      for (; j + 4 <= nt; j += 4) {
+        pstep(j, I0{}, sa, sb);
+        pstep(j + 1, I1{}, sb, sa);
+        pstep(j + 2, I2{}, sa, sb);
+        pstep(j + 3, I3{}, sb, sa);
+      }
+      if (j < nt) pstep(j, I0{}, sa, sb);
+      if (j + 1 < nt) pstep(j + 1, I1{}, sb, sa);
+      if (j + 2 < nt) pstep(j + 2, I2{}, sa, sb);
     }
-    if (j < nt) step(j, std::integral_constant<int, 0>{});
-    if (NS == 3 && j + 1 < nt) step(j + 1, std::integral_constant<int, 1>{});
   } else if constexpr (TL::PIPE == 3) {
     // ---- ping-pong schedule -------------------------------------------------
     // The NW waves form two groups of NW/2; wave i runs on SIMD i % 4, so with

@@ -118,6 +118,12 @@ int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float*
 int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int B, int H, int N, int d, int causal, float scale, int dtype, int variant);
 
+/*
+ * fa2_default_variant -- the variant index (>= 1) that variant 0 resolves to
+ * for this dtype, d and causal flag, or FA2_ERR_ARG / FA2_ERR_UNSUPPORTED.
+ */
+int fa2_default_variant(int dtype, int d, int causal);
+
 /* Number of tile variants (including the default, 0). */
 int fa2_num_variants(void);
 

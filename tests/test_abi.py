@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_named_call():
     names = declared_functions()
     for n in ["fa2_fwd", "fa2_fwd_fp16", "fa2_fwd_bf16", "fa2_fwd_variant", "fa2_fwd_check",
-              "fa2_status_string", "fa2_version", "fa2_num_variants", "fa2_variant_name"]:
+              "fa2_status_string", "fa2_version", "fa2_num_variants", "fa2_variant_name",
+              "fa2_default_variant"]:
         assert n in names
 
 
@@ -68,6 +69,12 @@ def test_status_strings_and_version(lib):
     assert fa2.variant_name(0) == "default"
     assert all(fa2.variant_name(i) for i in range(n))
     assert fa2.variant_name(n) is None and fa2.variant_name(-1) is None
+    for dt in (fa2.FA2_DTYPE_FP16, fa2.FA2_DTYPE_BF16):
+        for d in (64, 128):
+            for causal in (0, 1):
+                assert 1 <= fa2.default_variant(dt, d, causal) < n
+    assert fa2.lib().fa2_default_variant(5, 64, 0) == fa2.FA2_ERR_ARG
+    assert fa2.lib().fa2_default_variant(1, 96, 0) == fa2.FA2_ERR_UNSUPPORTED
 
 
 # Fake, 16-byte aligned, non-overlapping addresses: fa2_fwd_check only does
