@@ -131,10 +131,27 @@ __device__ __forceinline__ int chunk_swizzle(int row) {
 // lds + 16*l (buffer_load_dwordx4 ... lds; out-of-range lanes write zeros).
 // Kept in a device-only function: used directly in the kernel body, the
 // builtin makes the host compilation pass drop the kernel's launch stub.
+// With the builtin the compiler tracks the copy as an LDS write and makes
+// later LDS reads that it cannot tell apart from the destination (the
+// transpose reads) wait for every copy in flight.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset,
                                           int soffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, voffset,
                                            soffset, 0, 0);
+}
+// The same copy as inline assembly (Tile::ASMDMA): the compiler then does not
+// track it at all, and the kernel's own ordering is the only one: each wave
+// waits for its copies of a stage with s_waitcnt vmcnt, then a barrier
+// publishes the stage.  M0 holds the LDS destination; one wait state
+// separates its write from the copy.
+__device__ __forceinline__ void lds_dma16_asm(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset,
+                                              int soffset) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(r), "s"(soffset)
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(n) (n < 16) with expcnt and lgkmcnt left at their maxima.
@@ -164,9 +181,16 @@ struct Args {
 //   NW : waves per workgroup         QB : 32-query blocks per wave
 //   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
 //   PIPE: software-pipelined main loop (see below)
-template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0, int LOOK_ = 0>
+template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0, int LOOK_ = 0, int PRE_ = 0,
+          bool ASMDMA_ = false>
 struct Tile {
   static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  // ASMDMA (direct-copy loops): issue the global->LDS copies as inline
+  // assembly, invisible to the compiler's wait-count tracking
+  static constexpr bool ASMDMA = ASMDMA_;
+  // PRE (direct-copy loops): number of P.V operands (V^T fragments) read from
+  // LDS before the softmax, so that the P.V MFMAs can start without waiting
+  static constexpr int PRE = PRE_;
   // LOOK (direct-copy loops): keep this many score-MFMA operand reads in
   // flight ahead of the MFMAs (0: leave the order to the compiler)
   static constexpr int LOOK = LOOK_;
@@ -177,7 +201,7 @@ struct Tile {
   // PIPE 3: ping-pong between two wave groups in opposite phases;
   // PIPE 4 / 5: K and V copied straight from HBM into a 3- / 2-stage LDS ring
   // (buffer_load ... lds), swizzled unpadded rows;
-  // PIPE 6: 4-stage ring with the pipelined, interleaved loop of PIPE 2.
+  // PIPE 7: 4-stage ring with one barrier per two tiles.
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -205,9 +229,9 @@ void fa2_fwd_kernel(Args a) {
   // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
   // [key][d] K and V tiles
   constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
-  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 6: 4)
-  constexpr int NS = TL::PIPE == 4 ? 3 : (TL::PIPE == 6 ? 4 : 2);
-  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 6;
+  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7: 4)
+  constexpr int NS = TL::PIPE == 4 ? 3 : (TL::PIPE == 7 ? 4 : 2);
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7;
   constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 
@@ -319,8 +343,18 @@ void fa2_fwd_kernel(Args a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
-  const float c = a.c;
-  const bool c_neg = c < 0.f;
+  // A negative scale is folded into Q: c*s = (-c)*(-s) exactly (negating a
+  // 16-bit float flips its sign bit), so every loop below sees c >= 0, and
+  // the row max of c*s is c times the row max of s.
+  const bool c_neg = a.c < 0.f;
+  const float c = c_neg ? -a.c : a.c;
+  if (c_neg) {
+    const u32x4 sign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) qf[qb][dk] ^= sign;
+  }
   const int kbase = lr * KP + lh * 16;   // this lane's K fragment: row 32*kb + lr, chunk 2*dk + lh
   // V^T fragments come from row-major V through the LDS transpose read.  In
   // each 16-lane group g, lane (4e + c) fetches 4 elements of key row
@@ -348,20 +382,21 @@ void fa2_fwd_kernel(Args a) {
   };
 
   // online softmax of one tile of scores: updates m, l, returns P and alpha
-  auto softmax = [&](f32x16 (&s)[QB][KB], int key0, bool masked, u32x4 (&pf)[QB][KB][2],
-                     float (&alpha)[QB]) {
+  // s: f32x16[QB][NBK] scores of NBK 32-key blocks starting at key0,
+  // pf: u32x4[QB][NBK][2] packed P
+  auto softmax = [&](auto& s, int key0, bool masked, auto& pf, float (&alpha)[QB]) {
+    constexpr int NBK = sizeof(s[0]) / sizeof(f32x16);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float cc = c;
       float m_tile;
       if (masked) {
-        // tiles that cross the diagonal or the end of the sequence (and every
-        // tile when scale < 0): scale first, masked scores become -inf and
-        // exp2 gives exactly 0 for them
+        // tiles that cross the diagonal or the end of the sequence: scale
+        // first, masked scores become -inf and exp2 gives exactly 0 for them
         const int q = q_w + qb * 32 + lr;
         float e0 = -INFINITY, e1 = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -376,7 +411,7 @@ void fa2_fwd_kernel(Args a) {
         // c >= 0 here, so the tile max of c*s is c*max(s); two chains
         float e0 = s[qb][0][0], e1 = s[qb][0][1];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < NBK; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; r += 4) {
             e0 = fmaxf(e0, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
@@ -401,7 +436,7 @@ void fa2_fwd_kernel(Args a) {
       // to the input type for the P.V product.
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < NBK; ++kb) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           float p[8];
@@ -454,7 +489,7 @@ void fa2_fwd_kernel(Args a) {
     return CAUSAL && key0 > q_w + 32 * QB - 1;
   };
   auto tile_masked = [&](int key0) {   // tile crosses the diagonal or the end of the sequence
-    return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w) || c_neg;
+    return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
   };
 
   if constexpr (TL::PIPE == 0) {
@@ -517,8 +552,33 @@ void fa2_fwd_kernel(Args a) {
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
         const int dst = (wave * NIW + k) * 1024;
-        lds_dma16(kr, smem + S * TSZ + dst, dsrc[k], base);
-        lds_dma16(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
+        if constexpr (TL::ASMDMA) {
+          lds_dma16_asm(kr, smem + S * TSZ + dst, dsrc[k], base);
+          lds_dma16_asm(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
+        } else {
+          lds_dma16(kr, smem + S * TSZ + dst, dsrc[k], base);
+          lds_dma16(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
+        }
+      }
+    };
+    // The compiler does not count the copies (assembly) or does not relate
+    // them to Q, so it may believe the Q loads are still in flight inside the
+    // loop and wait for them (and so for every copy issued after them) there.
+    // Once the explicit wait has covered Q, pass the Q registers through an
+    // empty statement: the compiler's own wait for them lands here, before
+    // the loop.
+    auto q_ready = [&]() {
+      static_assert(QB * DK <= 16, "Q fragment count");
+      const u32x4* qq = &qf[0][0];
+      if constexpr (QB * DK == 4) {
+        asm volatile("" ::"v"(qq[0]), "v"(qq[1]), "v"(qq[2]), "v"(qq[3]));
+      } else if constexpr (QB * DK == 8) {
+        asm volatile("" ::"v"(qq[0]), "v"(qq[1]), "v"(qq[2]), "v"(qq[3]), "v"(qq[4]), "v"(qq[5]), "v"(qq[6]),
+                     "v"(qq[7]));
+      } else {
+        asm volatile("" ::"v"(qq[0]), "v"(qq[1]), "v"(qq[2]), "v"(qq[3]), "v"(qq[4]), "v"(qq[5]), "v"(qq[6]),
+                     "v"(qq[7]), "v"(qq[8]), "v"(qq[9]), "v"(qq[10]), "v"(qq[11]), "v"(qq[12]), "v"(qq[13]),
+                     "v"(qq[14]), "v"(qq[15]));
       }
     };
     // fragment addresses (see chunk_swizzle): K row 32*kb + lr, chunk 2*dk + lh;
@@ -569,10 +629,27 @@ void fa2_fwd_kernel(Args a) {
         if constexpr (VPM > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
       }
     };
+    // V^T operand of the P.V MFMA for (32-wide d block db, key block kb,
+    // 16-key step st) from V stage S
+    auto vread = [&](int db, int kb, int st, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int roff = S * TSZ + (32 * kb + 16 * st) * KROW;
+      const u32x2 lo = lds_read_tr16(smem + va[db][0] + roff);   // keys 4h + 0..3 of the step
+      const u32x2 hi = lds_read_tr16(smem + va[db][1] + roff);   // keys 8 + 4h + 0..3
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    constexpr int NPV = DB * KB * 2;            // P.V MFMAs per query block
+    constexpr int NPRE = TL::PRE < NPV ? TL::PRE : NPV;
+    typedef u32x4 PreOps[NPRE > 0 ? NPRE : 1];
+    // the first NPRE operands, in P.V order (db outer, then kb, then st)
+    auto vpre = [&](PreOps& pre, auto stage_tag) {
+#pragma unroll
+      for (int i = 0; i < NPRE; ++i) pre[i] = vread(i / (KB * 2), (i / 2) % KB, i % 2, stage_tag);
+    };
     // acc = alpha * acc when some row moved its reference, then O^T += V^T P^T
     // from V stage S
-    auto pv_st = [&](const u32x4 (&pfv)[QB][KB][2], const float (&al)[QB], auto stage_tag) {
-      constexpr int S = decltype(stage_tag)::value;
+    auto pv_st = [&](const u32x4 (&pfv)[QB][KB][2], const float (&al)[QB], const PreOps& pre,
+                     auto stage_tag) {
       bool moved = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) moved |= al[qb] != 1.f;
@@ -588,10 +665,10 @@ void fa2_fwd_kernel(Args a) {
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const int roff = S * TSZ + (32 * kb + 16 * st) * KROW;
-            const u32x2 lo = lds_read_tr16(smem + va[db][0] + roff);   // keys 4h + 0..3 of the step
-            const u32x2 hi = lds_read_tr16(smem + va[db][1] + roff);   // keys 8 + 4h + 0..3
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+            const int i = (db * KB + kb) * 2 + st;
+            u32x4 vf;
+            if (i < NPRE) vf = pre[i < NPRE ? i : 0];
+            else vf = vread(db, kb, st, stage_tag);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mfma(vf, pfv[qb][kb][st], acc[qb][db]);
           }
@@ -599,22 +676,37 @@ void fa2_fwd_kernel(Args a) {
       }
       if constexpr (TL::LOOK > 0) {
         // two transpose reads per MFMA, 2*LOOK reads ahead
-        constexpr int NM = DB * KB * 2;
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * TL::LOOK, 0);
+        constexpr int NM = NPV - NPRE;
+        constexpr int LA = TL::LOOK < NM ? TL::LOOK : NM;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LA, 0);
 #pragma unroll
-        for (int i = 0; i < NM - TL::LOOK; ++i) {
+        for (int i = 0; i < NM - LA; ++i) {
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, TL::LOOK, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, LA + NPRE, 0);
       }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    // one tile: scores, (prefetched P.V operands), softmax, P.V
+    auto tile = [&](int j, auto stage_tag) {
+      const int key0 = j * BC;
+      if (tile_skip(key0)) return;
+      f32x16 sv[QB][KB];
+      u32x4 pfv[QB][KB][2];
+      float al[QB];
+      PreOps pre;
+      scores_st(sv, stage_tag);
+      if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
+      if constexpr (NPRE > 0) vpre(pre, stage_tag);
+      softmax(sv, key0, tile_masked(key0), pfv, al);
+      pv_st(pfv, al, pre, stage_tag);
+    };
 
-    if constexpr (TL::PIPE != 6) {
+    if constexpr (TL::PIPE != 7) {
       auto step = [&](int j, auto stage_tag) {
         constexpr int S = decltype(stage_tag)::value;   // == j % NS
         // this wave's copies of tile j are done once at most the copies of the
@@ -628,21 +720,13 @@ void fa2_fwd_kernel(Args a) {
         // so stage (j-1)%NS == (j+NS-1)%NS may be refilled
         __syncthreads();
         if (j + NS - 1 < nt) dma(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
-        const int key0 = j * BC;
-        if (!tile_skip(key0)) {
-          f32x16 sv[QB][KB];
-          u32x4 pfv[QB][KB][2];
-          float al[QB];
-          scores_st(sv, stage_tag);
-          if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
-          softmax(sv, key0, tile_masked(key0), pfv, al);
-          pv_st(pfv, al, stage_tag);
-        }
+        tile(j, stage_tag);
       };
       dma(0, I0{});
       if (NS == 3 && nt > 1) dma(1, std::integral_constant<int, 1 % NS>{});
       // Q fragments were loaded before the copies: wait for them only
       if (NS == 3 && nt > 1) FA2_WAIT_VMCNT(4 * NIW); else FA2_WAIT_VMCNT(2 * NIW);
+      q_ready();
       int j = 0;
       for (; j + NS <= nt; j += NS) {
         step(j, I0{});
@@ -652,57 +736,33 @@ void fa2_fwd_kernel(Args a) {
       if (j < nt) step(j, I0{});
       if (NS == 3 && j + 1 < nt) step(j + 1, I1{});
     } else {
-      // Software-pipelined over a 4-stage ring: step j waits for tile j+1,
-      // refills stage (j+3)%4 (tile j-1's, finished by everyone at the
-      // barrier), then issues the score MFMAs of tile j+1 one by one between
-      // the softmax instructions of tile j, and finally P.V of tile j.
-      static_assert(NS == 4, "pipelined direct-copy loop uses 4 stages");
-      const int nclean = c_neg ? 0 : (CAUSAL ? min(q_wg, N) / BC : N / BC);   // tiles no wave masks
-      f32x16 sa[QB][KB], sb[QB][KB];   // scores of tiles j and j+1, roles alternate
-      auto pstep = [&](int j, auto stage_tag, f32x16 (&sc)[QB][KB], f32x16 (&sn)[QB][KB]) {
-        constexpr int S = decltype(stage_tag)::value;   // == j % 4
-        using SN = std::integral_constant<int, (S + 1) % 4>;
-        const bool next = j + 1 < nt;
-        // tile j+1 must have landed; tile j+2 may still be in flight
-        if (j + 2 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+      // 4-stage ring, one barrier per pair of tiles.  At the barrier before
+      // tiles j, j+1 (j even) every wave's copies of both have landed and
+      // every wave has finished tiles j-2, j-1, whose stages then receive
+      // tiles j+2, j+3.  Within a pair the waves drift freely.
+      static_assert(NS == 4, "pair-barrier loop uses 4 stages");
+      static_assert(4 * NIW < 64, "vmcnt range");
+      auto pair = [&](int j, auto stage_tag) {
+        constexpr int S = decltype(stage_tag)::value;   // == j % 4, even
+        // tiles j, j+1 must have landed; j+2, j+3 are not issued yet
+        FA2_WAIT_VMCNT(0);
         __syncthreads();
+        if (j + 2 < nt) dma(j + 2, std::integral_constant<int, (S + 2) % 4>{});
         if (j + 3 < nt) dma(j + 3, std::integral_constant<int, (S + 3) % 4>{});
-        const int key0 = j * BC;
-        u32x4 pfv[QB][KB][2];
-        float al[QB];
-        if (next && j < nclean) {
-          // steady state: tile j unmasked for every wave, tile j+1 needed by
-          // every wave; one basic block for the MFMAs and the softmax
-          scores_st(sn, SN{});
-          softmax(sc, key0, false, pfv, al);
-          order_scores(std::integral_constant<int, (TL::LOOK > 0 ? TL::LOOK : 4)>{},
-                       std::integral_constant<int, 0>{});
-          pv_st(pfv, al, stage_tag);
-        } else {
-          if (next && !tile_skip(key0 + BC)) scores_st(sn, SN{});
-          if (!tile_skip(key0)) {
-            softmax(sc, key0, tile_masked(key0), pfv, al);
-            pv_st(pfv, al, stage_tag);
-          }
-        }
+        tile(j, stage_tag);
+        if (j + 1 < nt) tile(j + 1, std::integral_constant<int, S + 1>{});
       };
       dma(0, I0{});
       if (nt > 1) dma(1, I1{});
-      if (nt > 2) dma(2, I2{});
-      // Q done (older than the copies); tile 0 landed: at most tiles 1, 2 in flight
-      if (nt > 2) FA2_WAIT_VMCNT(4 * NIW); else if (nt > 1) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
-      __syncthreads();
-      if (!tile_skip(0)) scores_st(sa, I0{});
+      FA2_WAIT_VMCNT(0);
+      q_ready();
       int j = 0;
       for (; j + 4 <= nt; j += 4) {
-        pstep(j, I0{}, sa, sb);
-        pstep(j + 1, I1{}, sb, sa);
-        pstep(j + 2, I2{}, sa, sb);
-        pstep(j + 3, I3{}, sb, sa);
+        pair(j, I0{});
+        pair(j + 2, I2{});
       }
-      if (j < nt) pstep(j, I0{}, sa, sb);
-      if (j + 1 < nt) pstep(j + 1, I1{}, sb, sa);
-      if (j + 2 < nt) pstep(j + 2, I2{}, sa, sb);
+      if (j < nt) pair(j, I0{});
+      if (j + 2 < nt) pair(j + 2, I2{});
     }
   } else if constexpr (TL::PIPE == 3) {
     // ---- ping-pong schedule -------------------------------------------------
@@ -791,7 +851,7 @@ void fa2_fwd_kernel(Args a) {
     // stage j&1).  K_{j+2} and V_{j+1} are fetched during the iteration and
     // written to K stage j&1 and V stage (j+1)&1, which nobody reads in
     // iteration j; one barrier per iteration publishes them.
-    const int nclean = c_neg ? 0 : (CAUSAL ? min(q_wg, N) / BC : N / BC);  // tiles no wave masks
+    const int nclean = CAUSAL ? min(q_wg, N) / BC : N / BC;  // tiles no wave masks
     const int nfast = min(nclean, nt - 1);
     load_k(0);
     load_v(0);
