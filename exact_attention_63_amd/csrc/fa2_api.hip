@@ -59,8 +59,10 @@ const Variant kVariants[] = {
     make_variant<Tile<8, 1, 4, 2, 5, 4>>("w8_q32_k128_dma2_look4"), // ... with 4 operand reads ahead
     make_variant<Tile<8, 1, 2, 2, 4, 0, 4>>("w8_q32_k64_dma3_pre4"),   // dma3 + 4 P.V operands read before the softmax
     make_variant<Tile<8, 1, 2, 2, 7, 0, 0>>("w8_q32_k64_dma4_pairs"),  // 4-stage ring, one barrier per 2 tiles
-    make_variant<Tile<8, 1, 2, 2, 7, 0, 4>>("w8_q32_k64_dma4_pairs_pre4"),
     make_variant<Tile<8, 1, 2, 2, 4, 0, 0, true>>("w8_q32_k64_dma3_asmcp"),   // dma3, copies as assembly
+    make_variant<Tile<8, 1, 2, 2, 9, 4>>("w8_q32_k64_dma4_pingpong_look4"),   // two wave groups in opposite phases
+    make_variant<Tile<8, 1, 2, 2, 4, 0, 0, false, 4>>("w8_q32_k64_dma3_asm4"),   // dma3, MFMA phases as assembly, 4 ahead
+    make_variant<Tile<8, 1, 2, 2, 9, 0, 0, false, 8>>("w8_q32_k64_dma4_pingpong_asm8"),  // ... MFMA phases as assembly, 8 ahead
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

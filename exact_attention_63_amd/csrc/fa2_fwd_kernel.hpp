@@ -157,6 +157,10 @@ __device__ __forceinline__ void lds_dma16_asm(__amdgpu_buffer_rsrc_t r, uint8_t*
 // s_waitcnt vmcnt(n) (n < 16) with expcnt and lgkmcnt left at their maxima.
 #define FA2_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
+// The two MFMA phases of a 64-key tile as inline-assembly blocks with a
+// fixed LDS-operand lookahead (generated by gen_mfma_phases.py).
+#include "fa2_mfma_phases.inc"
+
 // ds_read_b64_tr_b16: transpose read of 16-bit elements (see the V fragment
 // comment in the kernel for the lane mapping).
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
@@ -182,9 +186,14 @@ struct Args {
 //   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
 //   PIPE: software-pipelined main loop (see below)
 template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0, int LOOK_ = 0, int PRE_ = 0,
-          bool ASMDMA_ = false>
+          bool ASMDMA_ = false, int ASMPH_ = 0>
 struct Tile {
   static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  // ASMPH (direct-copy loops, d = 128, 32 rows per wave, 64-key tiles):
+  // issue each MFMA phase of a tile (16 score MFMAs; 16 P.V MFMAs) as one
+  // inline-assembly block that keeps ASMPH MFMAs' worth of LDS operand
+  // reads in flight and waits with exact counts (0: compiler-scheduled)
+  static constexpr int ASMPH = ASMPH_;
   // ASMDMA (direct-copy loops): issue the global->LDS copies as inline
   // assembly, invisible to the compiler's wait-count tracking
   static constexpr bool ASMDMA = ASMDMA_;
@@ -201,7 +210,8 @@ struct Tile {
   // PIPE 3: ping-pong between two wave groups in opposite phases;
   // PIPE 4 / 5: K and V copied straight from HBM into a 3- / 2-stage LDS ring
   // (buffer_load ... lds), swizzled unpadded rows;
-  // PIPE 7: 4-stage ring with one barrier per two tiles.
+  // PIPE 7: 4-stage ring with one barrier per two tiles;
+  // PIPE 9: 4-stage ring, two wave groups in opposite phases (ping-pong).
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -229,10 +239,12 @@ void fa2_fwd_kernel(Args a) {
   // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
   // [key][d] K and V tiles
   constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
-  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7: 4)
-  constexpr int NS = TL::PIPE == 4 ? 3 : (TL::PIPE == 7 ? 4 : 2);
-  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7;
+  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7 and 9: 4)
+  constexpr int NS = TL::PIPE == 4 ? 3 : ((TL::PIPE == 7 || TL::PIPE == 9) ? 4 : 2);
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7 || TL::PIPE == 9;
   constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
+  // hand-scheduled MFMA phases exist for d = 128, 32 rows per wave, 64-key tiles
+  constexpr int ASMPH = (DMA && D == 128 && QB == 1 && KB == 2) ? TL::ASMPH : 0;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
@@ -384,7 +396,7 @@ void fa2_fwd_kernel(Args a) {
   // online softmax of one tile of scores: updates m, l, returns P and alpha
   // s: f32x16[QB][NBK] scores of NBK 32-key blocks starting at key0,
   // pf: u32x4[QB][NBK][2] packed P
-  auto softmax = [&](auto& s, int key0, bool masked, auto& pf, float (&alpha)[QB]) {
+  auto softmax = [&](auto& s, int key0, bool masked, auto& pf, float (&alpha)[QB]) __attribute__((always_inline)) {
     constexpr int NBK = sizeof(s[0]) / sizeof(f32x16);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -598,8 +610,31 @@ void fa2_fwd_kernel(Args a) {
       va[db][1] = NS * TSZ + 8 * KROW + (vfb ^ (64 * db) ^ 32);
     }
     // S^T = K Q^T from K stage S
+    // LDS byte address of smem (the kernel's only LDS allocation)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
     auto scores_st = [&](f32x16 (&sv)[QB][KB], auto stage_tag) {
       constexpr int S = decltype(stage_tag)::value;
+      if constexpr (ASMPH > 0) {
+        const uint32_t k0 = lds0 + ka[0], k1 = lds0 + ka[1], k2 = lds0 + ka[2], k3 = lds0 + ka[3];
+        const uint32_t k4 = lds0 + ka[4], k5 = lds0 + ka[5], k6 = lds0 + ka[6], k7 = lds0 + ka[7];
+#define FA2_SCORES_OPERANDS                                                                                   \
+  : [s0] "=&v"(sv[0][0]), [s1] "=&v"(sv[0][1])                                                               \
+  : [ka0] "v"(k0), [ka1] "v"(k1), [ka2] "v"(k2), [ka3] "v"(k3), [ka4] "v"(k4), [ka5] "v"(k5), [ka6] "v"(k6), \
+    [ka7] "v"(k7), [q0] "v"(qf[0][0]), [q1] "v"(qf[0][1]), [q2] "v"(qf[0][2]), [q3] "v"(qf[0][3]),          \
+    [q4] "v"(qf[0][4]), [q5] "v"(qf[0][5]), [q6] "v"(qf[0][6]), [q7] "v"(qf[0][7]), [o0] "n"(S * TSZ),      \
+    [o1] "n"(S * TSZ + 32 * KROW)
+        if constexpr (BF16) {
+          static_assert(ASMPH == 4 || ASMPH == 8, "generated lookaheads: 4, 8");
+          if constexpr (ASMPH == 4) asm volatile(FA2_ASM_SCORES_BF16_L4 FA2_SCORES_OPERANDS : "memory", FA2_ASM_CLOBBERS_L4);
+          else asm volatile(FA2_ASM_SCORES_BF16_L8 FA2_SCORES_OPERANDS : "memory", FA2_ASM_CLOBBERS_L8);
+        } else {
+          static_assert(ASMPH == 4 || ASMPH == 8, "generated lookaheads: 4, 8");
+          if constexpr (ASMPH == 4) asm volatile(FA2_ASM_SCORES_F16_L4 FA2_SCORES_OPERANDS : "memory", FA2_ASM_CLOBBERS_L4);
+          else asm volatile(FA2_ASM_SCORES_F16_L8 FA2_SCORES_OPERANDS : "memory", FA2_ASM_CLOBBERS_L8);
+        }
+#undef FA2_SCORES_OPERANDS
+        return;
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -659,6 +694,28 @@ void fa2_fwd_kernel(Args a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[qb][db] *= al[qb];
       }
+      if constexpr (ASMPH > 0) {
+        constexpr int S = decltype(stage_tag)::value;
+        const uint32_t a0 = lds0 + va[0][0], b0 = lds0 + va[0][1], a1 = lds0 + va[1][0], b1 = lds0 + va[1][1];
+        const uint32_t a2 = lds0 + va[2][0], b2 = lds0 + va[2][1], a3 = lds0 + va[3][0], b3 = lds0 + va[3][1];
+#define FA2_PV_OPERANDS                                                                                         \
+  : [a0] "+v"(acc[0][0]), [a1] "+v"(acc[0][1]), [a2] "+v"(acc[0][2]), [a3] "+v"(acc[0][3])                   \
+  : [va0] "v"(a0), [vb0] "v"(b0), [va1] "v"(a1), [vb1] "v"(b1), [va2] "v"(a2), [vb2] "v"(b2), [va3] "v"(a3), \
+    [vb3] "v"(b3), [p00] "v"(pfv[0][0][0]), [p01] "v"(pfv[0][0][1]), [p10] "v"(pfv[0][1][0]),                \
+    [p11] "v"(pfv[0][1][1]), [o00] "n"(S * TSZ), [o01] "n"(S * TSZ + 16 * KROW),                              \
+    [o10] "n"(S * TSZ + 32 * KROW), [o11] "n"(S * TSZ + 48 * KROW)
+        if constexpr (BF16) {
+          static_assert(ASMPH == 4 || ASMPH == 8, "generated lookaheads: 4, 8");
+          if constexpr (ASMPH == 4) asm volatile(FA2_ASM_PV_BF16_L4 FA2_PV_OPERANDS : "memory", FA2_ASM_CLOBBERS_L4);
+          else asm volatile(FA2_ASM_PV_BF16_L8 FA2_PV_OPERANDS : "memory", FA2_ASM_CLOBBERS_L8);
+        } else {
+          static_assert(ASMPH == 4 || ASMPH == 8, "generated lookaheads: 4, 8");
+          if constexpr (ASMPH == 4) asm volatile(FA2_ASM_PV_F16_L4 FA2_PV_OPERANDS : "memory", FA2_ASM_CLOBBERS_L4);
+          else asm volatile(FA2_ASM_PV_F16_L8 FA2_PV_OPERANDS : "memory", FA2_ASM_CLOBBERS_L8);
+        }
+#undef FA2_PV_OPERANDS
+        return;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -706,7 +763,78 @@ void fa2_fwd_kernel(Args a) {
       pv_st(pfv, al, pre, stage_tag);
     };
 
-    if constexpr (TL::PIPE != 7) {
+    if constexpr (TL::PIPE == 9) {
+      // ---- ping-pong over the direct-copy ring --------------------------------
+      // The NW waves form two groups of NW/2; wave w runs on SIMD w % 4, so
+      // each SIMD holds one wave of each group.  Time is cut into half-steps
+      // separated by barriers.  In half-step h a group whose phase h - g is
+      // even runs its MFMA phase for tile t = (h - g) / 2 (P.V of tile t-1,
+      // then the scores of tile t); a group whose phase is odd runs the softmax
+      // of tile (h - g - 1) / 2.  The groups are always in opposite phases, so
+      // on every SIMD one wave feeds the MFMA pipe while the other keeps the
+      // VALU busy.  Tile u sits in stage u % 4: its K is read in half-steps 2u
+      // and 2u+1, its V in 2u+2 and 2u+3.  At the barrier opening half-step
+      // 2k every wave's copies of tile k have landed, and tile k-2 (last read
+      // in half-step 2k-1) is dead: its stage receives tile k+2.
+      static_assert(NW == 8, "ping-pong pairs the two waves of every SIMD");
+      const int grp = wave >> 2;
+      f32x16 sc[QB][KB];
+      u32x4 pf[QB][KB][2];
+      float al[QB];
+      PreOps pre;
+      const int nh = 2 * nt + 2;                    // half-steps
+      auto half = [&](int h, auto r_tag) {
+        constexpr int R = decltype(r_tag)::value;   // h % 8
+        if (h >= nh) return;
+        if constexpr (R % 2 == 0) {
+          const int k = h >> 1;
+          if (k >= 1 && k < nt) {
+            if (k + 1 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+          }
+        }
+        __syncthreads();
+        if constexpr (R % 2 == 0) {
+          const int k = h >> 1;
+          if (k >= 1 && k + 2 < nt) dma(k + 2, std::integral_constant<int, (R / 2 + 2) % 4>{});
+        }
+        if (grp == (R & 1)) {
+          // MFMA phase for tile t (stage ST)
+          constexpr int ST = (R / 2) % 4;
+          const int t = (h - grp) >> 1;
+          if (t >= 1 && !tile_skip((t - 1) * BC)) pv_st(pf, al, pre, std::integral_constant<int, (ST + 3) % 4>{});
+          if (t < nt && !tile_skip(t * BC)) {
+            scores_st(sc, std::integral_constant<int, ST>{});
+            if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
+          }
+        } else {
+          // softmax phase for tile t (stage SST); the wave's LDS port is idle
+          // here, so the first PRE V^T operands of its next P.V (tile t) are
+          // read now
+          constexpr int SST = (R & 1) ? ((R - 1) / 2) % 4 : (R / 2 + 3) % 4;
+          const int t = (h - grp - 1) >> 1;
+          if (h - grp >= 1 && t < nt && !tile_skip(t * BC)) {
+            if constexpr (NPRE > 0) vpre(pre, std::integral_constant<int, SST>{});
+            softmax(sc, t * BC, tile_masked(t * BC), pf, al);
+          }
+        }
+      };
+      dma(0, I0{});
+      if (nt > 1) dma(1, I1{});
+      if (nt > 2) dma(2, I2{});
+      // Q and tile 0 have landed when only the copies of tiles 1, 2 remain
+      if (nt > 2) FA2_WAIT_VMCNT(4 * NIW); else if (nt > 1) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+      q_ready();
+      for (int h = 0; h < nh; h += 8) {
+        half(h, I0{});
+        half(h + 1, I1{});
+        half(h + 2, I2{});
+        half(h + 3, I3{});
+        half(h + 4, std::integral_constant<int, 4>{});
+        half(h + 5, std::integral_constant<int, 5>{});
+        half(h + 6, std::integral_constant<int, 6>{});
+        half(h + 7, std::integral_constant<int, 7>{});
+      }
+    } else if constexpr (TL::PIPE != 7) {
       auto step = [&](int j, auto stage_tag) {
         constexpr int S = decltype(stage_tag)::value;   // == j % NS
         // this wave's copies of tile j are done once at most the copies of the
