@@ -68,13 +68,16 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Measured on MI355X (bench.py, same box, each variant twice, alternating):
 // non-causal d = 128 is fastest with 64-key tiles in a 3-stage direct-copy
-// ring and 4 operand reads ahead (variant 11); the causal workloads and
-// d = 64 with 128-key tiles in a 2-stage ring and 4 operand reads ahead
-// (variant 14).
+// ring and 4 operand reads ahead (variant 11); causal d = 128 and
+// non-causal d = 64 with 128-key tiles in a 2-stage ring and 4 operand reads
+// ahead (variant 14); causal d = 64 with 4-wave workgroups, two per CU, on a
+// 2-stage ring of 64-key tiles (variant 10: twice the workgroups balance the
+// triangular work, and the two workgroups of a CU are not held in step by
+// one barrier).
 int default_variant(int bf16, int d, int causal) {
   (void)bf16;
-  if (d == 128 && !causal) return 11;
-  return 14;
+  if (d == 128) return causal ? 14 : 11;
+  return causal ? 10 : 14;
 }
 
 // finite test on the bit pattern (independent of floating-point compile flags)
