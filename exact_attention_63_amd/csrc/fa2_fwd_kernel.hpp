@@ -29,19 +29,24 @@
 //     LDS reads; V^T fragments (keys along the MFMA k dimension) come from
 //     the gfx950 LDS transpose read ds_read_b64_tr_b16, whose lane mapping
 //     also realises the key renumbering above, so V needs no transpose in
-//     registers.  LDS rows are padded so that the lanes one LDS cycle serves
-//     fall on distinct banks of the 64 x 4-byte bank array: K pitch = 16 mod
-//     256 bytes (16-byte reads of 16 consecutive rows), V pitch = 64 mod 256
-//     bytes (transpose reads serve 32 lanes = 4 rows x 64 bytes per cycle) --
-//     the bank-conflict fix of blog chapter 4, done with padding instead of
-//     an XOR swizzle so that every unrolled access is a constant offset from
-//     one per-lane base address.
+//     registers.
+//   * The default loops copy K and V tiles straight from HBM into a ring of
+//     LDS stages (buffer_load ... lds), unpadded, with the 16-byte chunks of
+//     each row XOR-swizzled (chunk_swizzle) so that the lanes one LDS cycle
+//     serves fall on distinct banks of the 64 x 4-byte bank array -- the
+//     bank-conflict fix of blog chapter 4.  The older register-staged loops
+//     pad the rows instead (K pitch 16 mod 256 bytes, V pitch 64 mod 256).
 //   * Global reads and writes use buffer instructions with the head's extent
 //     as the range: rows past N read as zero and their stores are dropped, so
 //     ragged N needs no branches in the copy code.
 //   * Scale is folded into one FMA feeding exp2: p = 2^(s*c - m) with
 //     c = scale*log2(e) (blog chapter 6, FP instruction fusion); m, l are
-//     kept in the base-2 domain; LSE = (m + log2 l) * ln 2 at the end.
+//     kept in the base-2 domain; LSE = (m + log2 l) * ln 2 at the end.  A
+//     negative scale flips the sign of Q once, so c >= 0 in every loop.
+//   * The reference max of a row moves only when a tile's max exceeds it by
+//     more than kLazyRescale (the conditional rescale of the v4 diagram, in
+//     an exact form), so acc is rescaled only in the rare tiles where it
+//     moves.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -157,6 +162,15 @@ __device__ __forceinline__ void lds_dma16_asm(__amdgpu_buffer_rsrc_t r, uint8_t*
 // s_waitcnt vmcnt(n) (n < 16) with expcnt and lgkmcnt left at their maxima.
 #define FA2_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
+// Calls f(integral_constant<I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // The two MFMA phases of a 64-key tile as inline-assembly blocks with a
 // fixed LDS-operand lookahead (generated by gen_mfma_phases.py).
 #include "fa2_mfma_phases.inc"
@@ -197,8 +211,11 @@ struct Tile {
   // ASMDMA (direct-copy loops): issue the global->LDS copies as inline
   // assembly, invisible to the compiler's wait-count tracking
   static constexpr bool ASMDMA = ASMDMA_;
-  // PRE (direct-copy loops): number of P.V operands (V^T fragments) read from
-  // LDS before the softmax, so that the P.V MFMAs can start without waiting
+  // PRE (direct-copy loops): PIPE 4/5/7: number of P.V operands (V^T
+  // fragments) read from LDS before the softmax, so that the P.V MFMAs can
+  // start without waiting; PIPE 9: the same operands read during the softmax
+  // half-step; PIPE 10: MFMA operands read ahead in the threaded region
+  // (0 means 4)
   static constexpr int PRE = PRE_;
   // LOOK (direct-copy loops): keep this many score-MFMA operand reads in
   // flight ahead of the MFMAs (0: leave the order to the compiler)
@@ -211,7 +228,9 @@ struct Tile {
   // PIPE 4 / 5: K and V copied straight from HBM into a 3- / 2-stage LDS ring
   // (buffer_load ... lds), swizzled unpadded rows;
   // PIPE 7: 4-stage ring with one barrier per two tiles;
-  // PIPE 9: 4-stage ring, two wave groups in opposite phases (ping-pong).
+  // PIPE 9: 4-stage ring, two wave groups in opposite phases (ping-pong);
+  // PIPE 10: 4-stage ring, 32-key blocks, each wave's softmax threaded
+  // between its own MFMAs (see the loop).
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -239,9 +258,9 @@ void fa2_fwd_kernel(Args a) {
   // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
   // [key][d] K and V tiles
   constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
-  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7 and 9: 4)
-  constexpr int NS = TL::PIPE == 4 ? 3 : ((TL::PIPE == 7 || TL::PIPE == 9) ? 4 : 2);
-  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7 || TL::PIPE == 9;
+  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7, 9 and 10: 4)
+  constexpr int NS = TL::PIPE == 4 ? 3 : ((TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10) ? 4 : 2);
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10;
   constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
   // hand-scheduled MFMA phases exist for d = 128, 32 rows per wave, 64-key tiles
   constexpr int ASMPH = (DMA && D == 128 && QB == 1 && KB == 2) ? TL::ASMPH : 0;
@@ -763,7 +782,210 @@ void fa2_fwd_kernel(Args a) {
       pv_st(pfv, al, pre, stage_tag);
     };
 
-    if constexpr (TL::PIPE == 9) {
+    if constexpr (TL::PIPE == 10) {
+      // ---- 32-key blocks; softmax threaded between the wave's own MFMAs --------
+      // A single wave cannot keep the MFMA pipe full (measured: ≈36 cycles per
+      // back-to-back MFMA, ≈42 with operand reads and waits between them, 32
+      // when two waves interleave), so both waves of a SIMD must issue MFMAs
+      // all the time, and each wave's softmax has to run between its own
+      // MFMAs.  Block i = 2t + h is half h of key tile t (ring stage t % 4).
+      // Iteration i issues, as one region in a fixed order: the score MFMAs
+      // of block i+1 and the P.V MFMAs of block i-1 (16 MFMAs, their LDS
+      // operands read RA MFMAs ahead), with the softmax of block i cut into 16
+      // chunks placed after them; scheduling barriers keep that order.  The
+      // rescale of acc (rare) and the masking of a diagonal or tail block run
+      // before the region.  Barrier and copies as in the block pipeline: the
+      // barrier before the first read of tile t+1 (iteration 2t+1) publishes
+      // tile t+1 and frees the stage of tile t-1 (its V was last read in
+      // iteration 2t), which receives tile t+3.
+      static_assert(QB == 1 && KB == 2, "the block pipeline assumes 32 rows per wave and 64-key tiles");
+      constexpr int RA = TL::PRE > 0 ? TL::PRE : 4;      // MFMA operands read ahead
+      static_assert(RA >= 1, "read-ahead");
+      int n_eff = N;
+      if constexpr (CAUSAL) n_eff = min(N, q_wg + BR);
+      const int nb = (n_eff + 31) / 32;          // 32-key blocks this workgroup visits
+      auto live = [&](int i) { return i >= 0 && i < nb && !(CAUSAL && 32 * i > q_w + 31); };
+      auto masked = [&](int i) { return (32 * i + 32 > N) || (CAUSAL && 32 * i + 31 > q_w); };
+      auto koff_of = [&](int blk) { return ((blk >> 1) & 3) * TSZ + (blk & 1) * 32 * KROW; };
+      auto kread = [&](int dk, int koff) { return *(const u32x4*)(smem + (ka[dk] + koff)); };
+      auto vtread = [&](int db, int st, int voff) {
+        const u32x2 lo = lds_read_tr16(smem + (va[db][0] + voff) + 16 * st * KROW);
+        const u32x2 hi = lds_read_tr16(smem + (va[db][1] + voff) + 16 * st * KROW);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      auto rescale = [&](float al) {
+        if (__any(al != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[0][db] *= al;
+        }
+      };
+      auto mask_blk = [&](f32x16& sv, int i) {
+        const int q = q_w + lr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool vis = key < N && (!CAUSAL || key <= q);
+          sv[r] = vis ? sv[r] * c : -INFINITY;
+        }
+      };
+      f32x16 sbuf[2];
+      u32x4 pbuf[2][2];
+      float abuf[2];
+      // plain (unthreaded) pieces for the first and last blocks
+      auto sblk = [&](f32x16& sv, int koff) {
+        sv = f32x16{};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) sv = E::mfma(kread(dk, koff), qf[0][dk], sv);
+      };
+      auto pvblk = [&](const u32x4 (&p)[2], int voff) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) acc[0][db] = E::mfma(vtread(db, st, voff), p[st], acc[0][db]);
+      };
+      auto soft_plain = [&](const f32x16& sv, float cc, u32x4 (&p)[2], float& al) {
+        float e0 = fmaxf(sv[0], sv[1]), e1 = fmaxf(sv[2], sv[3]);
+#pragma unroll
+        for (int r = 4; r < 16; r += 4) {
+          e0 = fmaxf(e0, fmaxf(sv[r], sv[r + 1]));
+          e1 = fmaxf(e1, fmaxf(sv[r + 2], sv[r + 3]));
+        }
+        const float m_tile = max_halves(fmaxf(e0, e1)) * cc;
+        const float m_old = m_run[0];
+        const float m_new = (m_tile > m_old + kLazyRescale) ? m_tile : m_old;
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        al = __builtin_amdgcn_exp2f(m_old - m_use);
+        m_run[0] = m_new;
+        float rs0 = 0.f, rs1 = 0.f, pe[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          pe[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[u], cc, -m_use));
+          if (u & 1) rs1 += pe[u]; else rs0 += pe[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u >> 2][u & 3] = E::pack(pe[2 * u], pe[2 * u + 1]);
+        l_run[0] = l_run[0] * al + (rs0 + rs1);
+      };
+      // iteration i = 2t + H, i >= 1
+      auto iter = [&](int t, auto half_tag) {
+        constexpr int H = decltype(half_tag)::value;
+        constexpr int C = H, O = 1 - H;         // buffers of block i and of blocks i +- 1
+        const int i = 2 * t + H;
+        if constexpr (H == 1) {
+          if (t + 1 < nt) {
+            if (t + 2 < nt) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+            __syncthreads();
+            if (t + 3 < nt) {
+              switch ((t + 3) & 3) {
+                case 0: dma(t + 3, I0{}); break;
+                case 1: dma(t + 3, I1{}); break;
+                case 2: dma(t + 3, I2{}); break;
+                default: dma(t + 3, I3{}); break;
+              }
+            }
+          }
+        }
+        const bool prev = live(i - 1), cur = live(i);
+        if (!prev) return;                        // past this wave's diagonal
+        rescale(abuf[O]);
+        const int voff = koff_of(i - 1);
+        if (!cur) {                               // this wave's last P.V
+          pvblk(pbuf[O], voff);
+          return;
+        }
+        const bool msk = masked(i);
+        if (msk) mask_blk(sbuf[C], i);
+        const float cc = msk ? 1.f : c;
+        const int koff = koff_of(i + 1);          // past the end: stale LDS, never used
+        // ---- the threaded region ----
+        f32x16& sv = sbuf[C];
+        f32x16& sn = sbuf[O];
+        constexpr int NM = DK + 2 * DB;           // MFMAs of the region: DK score, 2*DB P.V
+        u32x4 opnd[NM];                           // their operands: K fragments, then V^T fragments
+        auto read_op = [&](auto m_tag) {
+          constexpr int M = decltype(m_tag)::value;
+          if constexpr (M < DK) opnd[M] = kread(M, koff);
+          else opnd[M] = vtread((M - DK) >> 1, (M - DK) & 1, voff);
+        };
+        auto mfma_op = [&](auto m_tag) {
+          constexpr int M = decltype(m_tag)::value;
+          if constexpr (M < DK) {
+            sn = M == 0 ? E::mfma(opnd[M], qf[0][M], f32x16{}) : E::mfma(opnd[M], qf[0][M], sn);
+          } else {
+            constexpr int db = (M - DK) >> 1, st = (M - DK) & 1;
+            acc[0][db] = E::mfma(opnd[M], pbuf[O][st], acc[0][db]);
+          }
+        };
+        float e0, e1, m_use, rs0 = 0.f, rs1 = 0.f, pe[16];
+        auto soft_chunk = [&](auto m_tag) {
+          constexpr int M = decltype(m_tag)::value;
+          if constexpr (M == 0) {
+            e0 = fmaxf(sv[0], sv[1]);
+            e1 = fmaxf(sv[2], sv[3]);
+            e0 = fmaxf(e0, fmaxf(sv[4], sv[5]));
+            e1 = fmaxf(e1, fmaxf(sv[6], sv[7]));
+          } else if constexpr (M == 1) {
+            e0 = fmaxf(e0, fmaxf(sv[8], sv[9]));
+            e1 = fmaxf(e1, fmaxf(sv[10], sv[11]));
+            e0 = fmaxf(e0, fmaxf(sv[12], sv[13]));
+            e1 = fmaxf(e1, fmaxf(sv[14], sv[15]));
+          } else if constexpr (M == 2) {
+            const float m_tile = max_halves(fmaxf(e0, e1)) * cc;
+            const float m_old = m_run[0];
+            const float m_new = (m_tile > m_old + kLazyRescale) ? m_tile : m_old;
+            m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            abuf[C] = __builtin_amdgcn_exp2f(m_old - m_use);
+            m_run[0] = m_new;
+          } else if constexpr (M >= 3 && M < 11) {
+            constexpr int u = 2 * (M - 3);
+            pe[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[u], cc, -m_use));
+            pe[u + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[u + 1], cc, -m_use));
+            rs0 += pe[u];
+            rs1 += pe[u + 1];
+          } else if constexpr (M >= 11 && M < 15) {
+            constexpr int u = 2 * (M - 11);
+            pbuf[C][u >> 2][u & 3] = E::pack(pe[2 * u], pe[2 * u + 1]);
+            pbuf[C][(u + 1) >> 2][(u + 1) & 3] = E::pack(pe[2 * u + 2], pe[2 * u + 3]);
+          } else if constexpr (M == 15) {
+            l_run[0] = l_run[0] * abuf[C] + (rs0 + rs1);
+          }
+        };
+        // slot m: MFMA m, softmax chunks [16m/NM, 16(m+1)/NM), operand read m+RA
+        static_assert(RA < NM, "read-ahead");
+        static_for<0, RA>([&](auto m) { read_op(m); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NM>([&](auto m) {
+          constexpr int M = decltype(m)::value;
+          mfma_op(m);
+          static_for<16 * M / NM, 16 * (M + 1) / NM>([&](auto c) { soft_chunk(c); });
+          if constexpr (M + RA < NM) read_op(std::integral_constant<int, M + RA>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      const int np = min(nt, 3);                  // tiles copied before the loop
+      dma(0, I0{});
+      if (np > 1) dma(1, I1{});
+      if (np > 2) dma(2, I2{});
+      if (np == 3) FA2_WAIT_VMCNT(4 * NIW); else if (np == 2) FA2_WAIT_VMCNT(2 * NIW); else FA2_WAIT_VMCNT(0);
+      q_ready();
+      __syncthreads();
+      // iteration 0: scores of blocks 0 and 1, softmax of block 0 (every wave
+      // sees key 0)
+      sblk(sbuf[0], 0);
+      sblk(sbuf[1], 32 * KROW);
+      {
+        const bool msk = masked(0);
+        if (msk) mask_blk(sbuf[0], 0);
+        soft_plain(sbuf[0], msk ? 1.f : c, pbuf[0], abuf[0]);
+      }
+      iter(0, I1{});
+      for (int t = 1; t < nt; ++t) {
+        iter(t, I0{});
+        iter(t, I1{});
+      }
+      // the P.V of the last block (iteration 2*nt)
+      iter(nt, I0{});
+    } else if constexpr (TL::PIPE == 9) {
       // ---- ping-pong over the direct-copy ring --------------------------------
       // The NW waves form two groups of NW/2; wave w runs on SIMD w % 4, so
       // each SIMD holds one wave of each group.  Time is cut into half-steps

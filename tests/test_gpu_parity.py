@@ -166,6 +166,22 @@ def test_every_variant_matches_oracle(causal, d, dtype):
         assert np.abs(l_i - outs[0][1]).max() <= 2 * TOL_LSE
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(64, "fp16"), (128, "bf16")])
+def test_every_variant_edge_shapes(causal, d, dtype):
+    """Every tile variant on one-row, one-past-a-tile and ragged sequences,
+    and with a negative scale (first block, tail masking and the sign fold
+    go through each variant's own loop)."""
+    cases = [(1, 1.0 / math.sqrt(d)), (65, 1.0 / math.sqrt(d)), (129, 1.0 / math.sqrt(d)), (129, -0.5)]
+    for n, scale in cases:
+        q, k, v = make_inputs(1, 2, n, d, dtype, seed=37 + n)
+        o_ref, l_ref = oracle_full(q, k, v, causal, scale)
+        for vi in range(1, fa2.num_variants()):
+            o, lse = gpu_forward(q, k, v, causal, scale, variant=vi)
+            check(o, lse, o_ref, l_ref, dtype, f"variant {vi} ({fa2.variant_name(vi)}) N={n} scale={scale}",
+                  output_rounding=scale < 0)
+
+
 # ------------------------------------------------------------ properties
 
 def test_deterministic_full_size():
