@@ -65,6 +65,7 @@ const Variant kVariants[] = {
     make_variant<Tile<8, 1, 2, 2, 9, 0, 0, false, 8>>("w8_q32_k64_dma4_pingpong_asm8"),  // ... MFMA phases as assembly, 8 ahead
     make_variant<Tile<4, 1, 2, 2, 5, 4>>("w4_q32_k64_dma2_look4"),   // 4 waves, 2 workgroups per CU, 4 operand reads ahead
     make_variant<Tile<8, 1, 2, 2, 10, 0, 4>>("w8_q32_k32_dma4_thread4"),   // softmax threaded between MFMAs, 4 operands ahead
+    make_variant<Tile<8, 1, 2, 2, 11, 4>>("w8_q32_k64_dma3_shift_look4"),  // waves 0-3 one phase ahead of waves 4-7
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

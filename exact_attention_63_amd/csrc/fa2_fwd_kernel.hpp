@@ -230,7 +230,8 @@ struct Tile {
   // PIPE 7: 4-stage ring with one barrier per two tiles;
   // PIPE 9: 4-stage ring, two wave groups in opposite phases (ping-pong);
   // PIPE 10: 4-stage ring, 32-key blocks, each wave's softmax threaded
-  // between its own MFMAs (see the loop).
+  // between its own MFMAs (see the loop);
+  // PIPE 11: 3-stage ring, waves 0-3 run one phase ahead of waves 4-7.
   static constexpr int PIPE = PIPE_;
   static constexpr int BR = NW * 32 * QB;  // query rows per workgroup
   static constexpr int BC = 32 * KB;       // keys per tile
@@ -258,9 +259,10 @@ void fa2_fwd_kernel(Args a) {
   // PIPE 4 (direct global->LDS copies): 3 stages of unpadded, XOR-swizzled
   // [key][d] K and V tiles
   constexpr int TSZ = BC * KROW;        // bytes of one unpadded K (or V) tile
-  // LDS stages of the direct-copy loops (PIPE 4: 3, PIPE 5: 2, PIPE 7, 9 and 10: 4)
-  constexpr int NS = TL::PIPE == 4 ? 3 : ((TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10) ? 4 : 2);
-  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10;
+  // LDS stages of the direct-copy loops (PIPE 4 and 11: 3, PIPE 5: 2, PIPE 7, 9 and 10: 4)
+  constexpr int NS = (TL::PIPE == 4 || TL::PIPE == 11) ? 3 : ((TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10) ? 4 : 2);
+  constexpr bool DMA = TL::PIPE == 4 || TL::PIPE == 5 || TL::PIPE == 7 || TL::PIPE == 9 || TL::PIPE == 10 ||
+                       TL::PIPE == 11;
   constexpr int SMEM = DMA ? NS * 2 * TSZ : 2 * STAGE;
   // hand-scheduled MFMA phases exist for d = 128, 32 rows per wave, 64-key tiles
   constexpr int ASMPH = (DMA && D == 128 && QB == 1 && KB == 2) ? TL::ASMPH : 0;
@@ -782,7 +784,63 @@ void fa2_fwd_kernel(Args a) {
       pv_st(pfv, al, pre, stage_tag);
     };
 
-    if constexpr (TL::PIPE == 10) {
+    if constexpr (TL::PIPE == 11) {
+      // ---- half-shifted wave groups over the 3-stage ring -------------------
+      // Waves 0-3 (group A) run one phase ahead of waves 4-7 (group B), which
+      // share their SIMDs (wave w runs on SIMD w % 4).  In step j group B runs
+      // the plain order: scores of tile j, softmax, P.V; group A runs the
+      // softmax of tile j (scores computed in step j-1), P.V of tile j, then
+      // the scores of tile j+1.  With one barrier per step, one wave's softmax
+      // then meets the other wave's MFMAs at the start of the step, and both
+      // waves issue MFMAs in its second part.  Group A reads tile j+1 in step
+      // j, so every wave waits for its copies of tile j+1 before the barrier
+      // of step j (one step of copy lead time); after that barrier the stage
+      // of tile j-1 (last read in step j-1) receives tile j+2.
+      static_assert(NS == 3 && NW == 8, "half-shifted groups use the 8-wave 3-stage ring");
+      const bool ahead = wave < 4;
+      f32x16 sa[QB][KB];                          // group A: scores of the next tile
+      auto step = [&](int j, auto stage_tag) {
+        constexpr int S = decltype(stage_tag)::value;   // == j % 3
+        if (j >= 1) {
+          FA2_WAIT_VMCNT(0);
+          __syncthreads();
+        }
+        if (j + 2 < nt) dma(j + 2, std::integral_constant<int, (S + 2) % 3>{});
+        const int key0 = j * BC;
+        if (ahead) {
+          if (!tile_skip(key0)) {
+            u32x4 pfv[QB][KB][2];
+            float al[QB];
+            PreOps pre;
+            softmax(sa, key0, tile_masked(key0), pfv, al);
+            pv_st(pfv, al, pre, stage_tag);
+          }
+          if (j + 1 < nt && !tile_skip(key0 + BC)) {
+            scores_st(sa, std::integral_constant<int, (S + 1) % 3>{});
+            if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
+          }
+        } else {
+          tile(j, stage_tag);
+        }
+      };
+      dma(0, I0{});
+      if (nt > 1) dma(1, I1{});
+      FA2_WAIT_VMCNT(0);
+      q_ready();
+      __syncthreads();
+      if (ahead && !tile_skip(0)) {
+        scores_st(sa, I0{});
+        if constexpr (TL::LOOK > 0) order_scores(std::integral_constant<int, TL::LOOK>{}, I0{});
+      }
+      int j = 0;
+      for (; j + 3 <= nt; j += 3) {
+        step(j, I0{});
+        step(j + 1, I1{});
+        step(j + 2, I2{});
+      }
+      if (j < nt) step(j, I0{});
+      if (j + 1 < nt) step(j + 1, I1{});
+    } else if constexpr (TL::PIPE == 10) {
       // ---- 32-key blocks; softmax threaded between the wave's own MFMAs --------
       // A single wave cannot keep the MFMA pipe full (measured: ≈36 cycles per
       // back-to-back MFMA, ≈42 with operand reads and waits between them, 32
