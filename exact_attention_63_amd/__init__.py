@@ -1,4 +1,4 @@
-"""Exact attention forward (FlashAttention-2 style) on AMD MI355X.
+"""Exact attention (FlashAttention-2 style) forward and backward on AMD MI355X.
 
 A thin ctypes binding over ``libfa2.so``, the C ABI declared in
 ``include/fa2.h``.  PyTorch only provides device memory and the stream; every
@@ -7,6 +7,7 @@ fallback: when the library is missing or no GPU is present, calls raise.
 
     from exact_attention_63_amd import forward
     o, lse = forward(q, k, v, causal=False)        # q, k, v: [B, H, N, d] cuda fp16/bf16
+    dq, dk, dv, delta = backward(q, k, v, o, lse, do, causal=False)
 """
 
 from __future__ import annotations
@@ -16,7 +17,7 @@ import math
 import os
 
 __all__ = [
-    "forward", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "forward", "backward", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
     "default_variant",
     "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
     "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
@@ -49,6 +50,10 @@ EXPORTS = {
     "fa2_fwd": (_I, _FWD12 + [_I]),
     "fa2_fwd_variant": (_I, _FWD12 + [_I, _I]),
     "fa2_fwd_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+    "fa2_bwd": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P, _I]),
+    "fa2_bwd_fp16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
+    "fa2_bwd_bf16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
+    "fa2_bwd_check": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _I]),
     "fa2_default_variant": (_I, [_I, _I, _I]),
     "fa2_num_variants": (_I, []),
     "fa2_variant_name": (ctypes.c_char_p, [_I]),
@@ -164,3 +169,56 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
     if rc != FA2_OK:
         raise Fa2Error(rc, "fa2_fwd_variant")
     return out, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, *,
+             dq=None, dk=None, dv=None, delta=None):
+    """Attention backward: returns (dQ, dK, dV in q's dtype, delta [B,H,N] float32).
+
+    q, k, v, o, do: contiguous CUDA tensors [B, H, N, d] of one dtype (fp16 or
+    bf16), d in {64, 128}; o and lse [B, H, N] float32 are the forward pass's
+    outputs for q, k, v with the same causal flag and scale (default
+    1/sqrt(d)).  delta receives rowsum(dO * O).  The three kernels are
+    enqueued on the current stream of q's device; the call does not
+    synchronise.  dq, dk, dv, delta may pass preallocated outputs.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d]; got {tuple(q.shape)}")
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape {tuple(q.shape)}; got {tuple(t.shape)}")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's dtype")
+    code = _dtype_code(q.dtype)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 tensor [B, H, N]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous() \
+            or delta.device != q.device:
+        raise ValueError("delta must be a contiguous float32 tensor [B, H, N] on q's device")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib().fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                           B, H, N, d, int(bool(causal)), float(scale), stream, code)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, "fa2_bwd")
+    return dq, dk, dv, delta

@@ -1,7 +1,8 @@
 // fa2_api.hip -- host side of the C ABI declared in include/fa2.h: argument
 // validation, the tile-variant table and the kernel launch.
 //
-// The call enqueues one kernel and returns.  It allocates nothing (the method
+// A forward call enqueues one kernel, a backward call three; each returns
+// after enqueueing.  It allocates nothing (the method
 // needs O(N) memory: only the inputs and outputs), keeps no state besides
 // constant tables, and validates every argument before touching the HIP
 // runtime, so an invalid call has no effect.
@@ -10,6 +11,7 @@
 
 #include "fa2.h"
 #include "fa2_fwd_kernel.hpp"
+#include "fa2_bwd_kernel.hpp"
 
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -159,6 +161,128 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return FA2_OK;
 }
 
+
+// ---- backward ---------------------------------------------------------------
+
+using fa2::BwdArgs;
+using fa2::BwdTile;
+
+typedef void (*bwd_fn)(BwdArgs);
+typedef void (*delta_fn)(BwdArgs, long long);
+
+// dK/dV kernel: 4 waves (128 keys) per workgroup, one wave per SIMD (K, V
+// rows, two accumulators and two score blocks need more than 256 VGPRs).
+// dQ kernel: 8 waves (256 queries) per workgroup, two waves per SIMD.
+using KvTile = BwdTile<4, 1>;
+using QTile = BwdTile<8, 2>;
+
+struct BwdKernels {
+  delta_fn delta[2][2];        // [bf16][d == 128]
+  bwd_fn dkdv[2][2][2];        // [bf16][d == 128][causal]
+  bwd_fn dq[2][2][2];
+};
+
+template <bool BF16, int D>
+constexpr void fill_bwd(BwdKernels& t) {
+  t.delta[BF16][D == 128] = fa2::fa2_bwd_delta_kernel<BF16, D>;
+  t.dkdv[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_kernel<BF16, D, false, KvTile>;
+  t.dkdv[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_kernel<BF16, D, true, KvTile>;
+  t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
+  t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
+}
+
+BwdKernels make_bwd_kernels() {
+  BwdKernels t{};
+  fill_bwd<false, 64>(t);
+  fill_bwd<false, 128>(t);
+  fill_bwd<true, 64>(t);
+  fill_bwd<true, 128>(t);
+  return t;
+}
+
+const BwdKernels kBwd = make_bwd_kernels();
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
+              const void* dout, const void* dq, const void* dk, const void* dv, const void* delta,
+              int B, int H, int N, int d, int causal, float scale, int dtype) {
+  if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_ARG;
+  if (!finite_bits(scale)) return FA2_ERR_ARG;
+  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return kEmpty;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA2_ERR_NULL;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if ((uint64_t)N * (uint64_t)d * 2u >= (1ull << 32)) return FA2_ERR_SHAPE;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  if (bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  const uint64_t elems = bh * (uint64_t)N * (uint64_t)d;
+  if (elems >= (1ull << 62)) return FA2_ERR_SHAPE;
+  // grids: 128-key blocks, and the D kernel's 256-lane blocks of 8 elements per lane
+  if (((uint64_t)N + 127) / 128 * bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if ((elems / 8 + 255) / 256 > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15u)
+    return FA2_ERR_ALIGN;
+  const size_t tb = (size_t)elems * 2u;
+  const size_t lb = (size_t)(bh * (uint64_t)N) * 4u;
+  const void* in[6] = {q, k, v, o, lse, dout};
+  const size_t inb[6] = {tb, tb, tb, tb, lb, tb};
+  const void* out[4] = {dq, dk, dv, delta};
+  const size_t outb[4] = {tb, tb, tb, lb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], outb[i], in[j], inb[j])) return FA2_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], outb[i], out[j], outb[j])) return FA2_ERR_ALIAS;
+  }
+  return FA2_OK;
+}
+
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
+            int causal, float scale, hipStream_t stream, int dtype) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype);
+  if (st == kEmpty) return FA2_OK;
+  if (st != FA2_OK) return st;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  const int bf16 = dtype == FA2_DTYPE_BF16;
+  const int big = d == 128;
+
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.BH = (int)bh;
+  a.N = N;
+  a.c = scale * 1.4426950408889634f;
+  a.scale = scale;
+
+  // D = rowsum(dO * O): one lane per 8 elements
+  const long long rows = (long long)(bh * (uint64_t)N);
+  const uint64_t lanes = (uint64_t)rows * (uint64_t)(d / 8);
+  a.nblk = 0;
+  hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+
+  a.nblk = (N + KvTile::BR - 1) / KvTile::BR;
+  hipLaunchKernelGGL(kBwd.dkdv[bf16][big][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
+                     dim3(KvTile::THREADS), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+
+  a.nblk = (N + QTile::BR - 1) / QTile::BR;
+  hipLaunchKernelGGL(kBwd.dq[bf16][big][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
+                     dim3(QTile::THREADS), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+  return FA2_OK;
+}
+
 }  // namespace
 
 FA2_EXPORT int fa2_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -192,6 +316,36 @@ FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const 
   return st == kEmpty ? FA2_OK : st;
 }
 
+FA2_EXPORT int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                       int N, int d, int causal, float scale, hipStream_t stream, int dtype) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype);
+}
+
+FA2_EXPORT int fa2_bwd_fp16(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* delta, int B, int H, int N, int d, int causal, float scale,
+                            hipStream_t stream) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream,
+                 FA2_DTYPE_FP16);
+}
+
+FA2_EXPORT int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* delta, int B, int H, int N, int d, int causal, float scale,
+                            hipStream_t stream) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream,
+                 FA2_DTYPE_BF16);
+}
+
+FA2_EXPORT int fa2_bwd_check(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* dq, const void* dk,
+                             const void* dv, const float* delta, int B, int H, int N, int d,
+                             int causal, float scale, int dtype) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype);
+  return st == kEmpty ? FA2_OK : st;
+}
+
 FA2_EXPORT int fa2_default_variant(int dtype, int d, int causal) {
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_ARG;
@@ -214,7 +368,7 @@ FA2_EXPORT const char* fa2_status_string(int status) {
     case FA2_ERR_UNSUPPORTED: return "unsupported head dimension: d must be 64 or 128";
     case FA2_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA2_ERR_ARG: return "invalid argument: scale, causal, dtype or variant";
-    case FA2_ERR_ALIAS: return "the output overlaps an input or the other output";
+    case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }

@@ -62,7 +62,7 @@ enum fa2_status {
     FA2_ERR_UNSUPPORTED = -3, /* d is not 64 or 128                                         */
     FA2_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                    */
     FA2_ERR_ARG = -5,         /* scale not finite, causal not 0/1, bad dtype or variant     */
-    FA2_ERR_ALIAS = -6,       /* o overlaps q, k, v or lse, or lse overlaps q, k or v       */
+    FA2_ERR_ALIAS = -6,       /* an output overlaps an input or another output              */
     FA2_ERR_LAUNCH = -7       /* the HIP runtime reported an error when launching           */
 };
 
@@ -117,6 +117,60 @@ int fa2_fwd_variant(const void* q, const void* k, const void* v, void* o, float*
  */
 int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int B, int H, int N, int d, int causal, float scale, int dtype, int variant);
+
+/*
+ * fa2_bwd -- the backward pass: gradients of the forward pass's O with
+ * respect to q, k and v, given the upstream gradient dO.
+ *
+ * The pages name the backward pass as the step after the forward one
+ * ("FlashAttention v4 Blackwell pipeline co-design" diagram: its list of v4
+ * directions and the backward note under its pseudo-code panel, which aim to
+ * remove the atomic accumulation of dQ; a snippet of the search-result page
+ * for the FlashAttention-2 paper lists backward support) but print no
+ * formulas.  The gradients are those of the forward definition above.  With
+ * S = scale * Q K^T (masked as in the forward pass), P = exp(S - LSE) (the
+ * softmax rows, recomputed from the saved LSE), D_i = sum_t dO[i,t] O[i,t]:
+ *
+ *     dV = P^T dO      dS = P * (dO V^T - D)      dQ = scale * dS K      dK = scale * dS^T Q
+ *
+ *   q, k, v  [in]  device, [B,H,N,d] fp16 or bf16 (dtype), 16-byte aligned
+ *   o        [in]  device, [B,H,N,d]: the forward pass's output for q, k, v
+ *   lse      [in]  device, [B,H,N] float32: the forward pass's LSE
+ *   dout     [in]  device, [B,H,N,d]: the upstream gradient dO
+ *   dq, dk, dv [out] device, [B,H,N,d] same dtype (rounded to nearest even)
+ *   delta    [out] device, [B,H,N] float32: D_i = rowsum(dO * O), in fp32
+ *                  (also consumed by the call itself)
+ *   B, H, N, d, causal, scale, stream, dtype: as for fa2_fwd; scale and
+ *                  causal must be the values the forward pass used.
+ *
+ * Every pointer is 16-byte aligned and owned by the caller; no output may
+ * overlap an input or another output.  The call enqueues three kernels on
+ * stream (D, then dK and dV, then dQ) and allocates nothing: dQ is computed
+ * by its own kernel over query blocks instead of by atomic adds across key
+ * blocks, so results are deterministic.  Validation and error codes as for
+ * fa2_fwd (NULL, shape, d, alignment, overlap, argument), before any HIP
+ * call; on failure nothing is launched and no output is written.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float* delta,
+            int B, int H, int N, int d, int causal, float scale, hipStream_t stream, int dtype);
+
+/* fa2_bwd_fp16 / fa2_bwd_bf16 -- fa2_bwd for one element type. */
+int fa2_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta,
+                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta,
+                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * fa2_bwd_check -- run exactly the argument validation of fa2_bwd and return
+ * its status, without launching anything or calling the HIP runtime.
+ */
+int fa2_bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, const void* dq, const void* dk, const void* dv,
+                  const float* delta, int B, int H, int N, int d, int causal, float scale,
+                  int dtype);
 
 /*
  * fa2_default_variant -- the variant index (>= 1) that variant 0 resolves to

@@ -1,7 +1,7 @@
 """The C-ABI library: it loads, exports every function include/fa2.h declares,
 and its host-side validation returns the documented status for each invalid
-argument.  No GPU is needed: validation is exercised through fa2_fwd_check,
-which never calls the HIP runtime.
+argument.  No GPU is needed: validation is exercised through fa2_fwd_check and
+fa2_bwd_check, which never call the HIP runtime.
 """
 
 import ctypes
@@ -35,7 +35,7 @@ def test_header_declares_the_named_call():
     names = declared_functions()
     for n in ["fa2_fwd", "fa2_fwd_fp16", "fa2_fwd_bf16", "fa2_fwd_variant", "fa2_fwd_check",
               "fa2_status_string", "fa2_version", "fa2_num_variants", "fa2_variant_name",
-              "fa2_default_variant"]:
+              "fa2_default_variant", "fa2_bwd", "fa2_bwd_fp16", "fa2_bwd_bf16", "fa2_bwd_check"]:
         assert n in names
 
 
@@ -151,3 +151,63 @@ def test_python_binding_rejects_cpu_tensors(lib):
         fa2.forward(x, x, x)
     with pytest.raises(ValueError):
         fa2.forward(x.float(), x.float(), x.float())
+
+
+# ------------------------------------------------------------ backward validation
+
+DO, DQ, DK, DV, DL = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+
+def bchk(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, H=3, N=100, d=64,
+         causal=0, scale=0.125, dtype=1):
+    return fa2.lib().fa2_bwd_check(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, N, d, causal, scale,
+                                   dtype)
+
+
+def test_bwd_valid_arguments_pass(lib):
+    assert bchk() == fa2.FA2_OK
+    assert bchk(d=128, causal=1, dtype=0) == fa2.FA2_OK
+    assert bchk(scale=0.0) == fa2.FA2_OK and bchk(scale=-1.5) == fa2.FA2_OK
+    # inputs are read only: they may alias each other
+    assert bchk(k=Q, v=Q, do=O) == fa2.FA2_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa2.FA2_ERR_NULL), (dict(o=None), fa2.FA2_ERR_NULL),
+    (dict(lse=None), fa2.FA2_ERR_NULL), (dict(do=None), fa2.FA2_ERR_NULL),
+    (dict(dq=None), fa2.FA2_ERR_NULL), (dict(dk=None), fa2.FA2_ERR_NULL),
+    (dict(dv=None), fa2.FA2_ERR_NULL), (dict(delta=None), fa2.FA2_ERR_NULL),
+    (dict(B=-1), fa2.FA2_ERR_SHAPE), (dict(N=-2), fa2.FA2_ERR_SHAPE),
+    (dict(N=1 << 24, d=128), fa2.FA2_ERR_SHAPE),
+    (dict(d=96), fa2.FA2_ERR_UNSUPPORTED), (dict(d=256), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(do=DO + 8), fa2.FA2_ERR_ALIGN), (dict(delta=DL + 4), fa2.FA2_ERR_ALIGN),
+    (dict(dk=DK + 2), fa2.FA2_ERR_ALIGN),
+    (dict(scale=math.nan), fa2.FA2_ERR_ARG), (dict(causal=3), fa2.FA2_ERR_ARG),
+    (dict(dtype=9), fa2.FA2_ERR_ARG),
+    (dict(dq=Q), fa2.FA2_ERR_ALIAS), (dict(dk=DO + 4096), fa2.FA2_ERR_ALIAS),
+    (dict(dv=L), fa2.FA2_ERR_ALIAS), (dict(delta=O + 1024), fa2.FA2_ERR_ALIAS),
+    (dict(dv=DQ + 16), fa2.FA2_ERR_ALIAS), (dict(delta=DK), fa2.FA2_ERR_ALIAS),
+])
+def test_bwd_invalid_arguments(lib, kw, status):
+    assert bchk(**kw) == status
+
+
+def test_bwd_empty_problem_is_a_noop(lib):
+    none = dict(q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None, delta=None)
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        assert bchk(**none, **kw) == fa2.FA2_OK
+
+
+def test_bwd_adjacent_outputs_do_not_alias(lib):
+    B, H, N, d = 2, 3, 100, 64
+    tbytes = B * H * N * d * 2
+    assert bchk(dq=DQ, dk=DQ + tbytes, dv=DQ + 2 * tbytes) == fa2.FA2_OK
+    assert bchk(dq=DQ, dk=DQ + tbytes - 16) == fa2.FA2_ERR_ALIAS
+
+
+def test_python_backward_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        fa2.backward(x, x, x, x, lse, x)

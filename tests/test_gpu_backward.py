@@ -1,0 +1,212 @@
+"""GPU parity of the backward pass (dQ, dK, dV, D) against the fp64 CPU oracle.
+
+The HIP backward receives O rounded to the input dtype and LSE rounded to
+fp32, both taken from the fp64 oracle forward pass (never from the HIP path),
+plus the seeded dO.  Its outputs are compared with ``oracle.attention_backward``
+(fp64, from Q, K, V and dO alone).
+
+Tolerance.  The pages give none for gradients, so each element gets a bound
+derived from the arithmetic the kernels perform, with u the unit roundoff of
+the input dtype (bf16 2^-8, fp16 2^-11):
+  * P is recomputed in fp32 (relative error ~1e-6, far below u) and rounded
+    to the dtype for dV = P^T dO:      |dV err| <= u (P^T |dO|) + u |dV|;
+  * D = rowsum(dO * O) uses the rounded O: |D err|_i <= u a_i with
+    a_i = sum_t |dO_it| |O_it|;
+  * dS = P (dP - D) is rounded to the dtype for the two products:
+    |dS err|_ij <= u (|dS_ij| + P_ij a_i) =: E_ij;
+  * |dK err| <= |scale| (E^T |Q|) + u |dK|,  |dQ err| <= |scale| (E |K|) + u |dQ|
+    (the last term is the final rounding to the dtype).
+Each element must satisfy |gpu - oracle| <= 2 * bound + 1e-5 * max|oracle|
+(the factor 2 covers second-order terms and fp32 accumulation, whose error is
+~d * 2^-24 relative).  D itself is fp32: |D err| <= u a_i + 1e-5 a_i.
+A wrong index, sign or operand produces errors of the size of the terms
+themselves, orders of magnitude above these bounds.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_63_amd as fa2
+import oracle
+from workloads import WORKLOADS, make_grad_output, make_inputs, to_f64, workload_grad_output, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    fa2.lib()
+
+
+def oracle_forward_inputs(q64, k64, v64, causal, scale, dtype):
+    """The oracle's O (rounded to dtype) and LSE (rounded to fp32) as CPU tensors."""
+    o, lse = oracle.attention_3pass(q64, k64, v64, causal, scale)
+    td = torch.float16 if dtype == "fp16" else torch.bfloat16
+    return torch.from_numpy(o).to(td), torch.from_numpy(lse).to(torch.float32)
+
+
+def head_bounds(q, k, v, o_r, do, causal, scale, dtype, ref):
+    """Elementwise error bounds for one head (fp64 arrays [N, d]); ref = oracle (dq, dk, dv, delta)."""
+    u = UNIT[dtype]
+    n = q.shape[0]
+    vis = oracle.visible_mask(np.arange(n), n, causal)
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    dq, dk, dv, delta = ref
+    ds = p * ((do @ v.T) - delta[:, None])
+    a = (np.abs(do) * np.abs(o_r)).sum(axis=1)
+    E = u * (np.abs(ds) + p * a[:, None])
+    b_dv = u * (p.T @ np.abs(do)) + u * np.abs(dv)
+    b_dk = abs(scale) * (E.T @ np.abs(q)) + u * np.abs(dk)
+    b_dq = abs(scale) * (E @ np.abs(k)) + u * np.abs(dq)
+    b_delta = (u + 1e-5) * a
+    return b_dq, b_dk, b_dv, b_delta
+
+
+def compare(name, got, ref, bound):
+    err = np.abs(got - ref)
+    tol = 2.0 * bound + 1e-5 * max(np.abs(ref).max(), 1e-30)
+    ratio = (err / tol).max() if err.size else 0.0
+    print(f"  {name}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
+          f"worst err/tol={ratio:.3f}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    assert ratio <= 1.0, f"{name}: error above the derived bound (worst err/tol {ratio:.3f})"
+
+
+def gpu_backward(q, k, v, o, lse, do, causal, scale):
+    t = [x.cuda() for x in (q, k, v, o, lse, do)]
+    dq, dk, dv, delta = fa2.backward(*t, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv, delta
+
+
+def check_heads(what, q, k, v, o_r, do, out, causal, scale, dtype, heads):
+    """Compare the GPU outputs of the listed (b, h) heads with the oracle, element by element."""
+    q64, k64, v64, o64, do64 = (to_f64(x) for x in (q, k, v, o_r, do))
+    g = [to_f64(x) for x in out]
+    for b, h in heads:
+        ref = oracle.attention_backward(q64[b, h], k64[b, h], v64[b, h], do64[b, h], causal, scale)
+        bnd = head_bounds(q64[b, h], k64[b, h], v64[b, h], o64[b, h], do64[b, h], causal, scale, dtype, ref)
+        print(f"{what} head ({b},{h})", flush=True)
+        for name, gi, ri, bi in zip(("dQ", "dK", "dV", "D"), g, ref, bnd):
+            compare(name, gi[b, h], ri, bi)
+
+
+def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0, key_offset=None):
+    q, k, v = make_inputs(B, H, N, d, dtype, seed, sigma, key_offset)
+    do = make_grad_output(B, H, N, d, dtype, seed)
+    q64, k64, v64 = (to_f64(x) for x in (q, k, v))
+    o_r, lse = oracle_forward_inputs(q64, k64, v64, causal, scale, dtype)
+    out = gpu_backward(q, k, v, o_r, lse, do, causal, scale)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    check_heads(what, q, k, v, o_r, do, out, causal, scale, dtype, heads)
+
+
+# ------------------------------------------------------------ small shapes, every element
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 31, 64, 65, 127, 129, 200, 513])
+def test_backward_edge_shapes(N, d, causal, dtype):
+    """Ragged N (partial query and key tiles, partial workgroups), single rows."""
+    seed = 20_000 + N * 8 + (d == 128) * 4 + causal * 2 + (dtype == "bf16")
+    run_case(f"N={N} d={d} causal={causal} {dtype}", 1, 2, N, d, dtype, causal, 1.0 / math.sqrt(d), seed)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_scales(scale, causal):
+    """Zero and negative scales (P uniform over the visible keys; sign flips)."""
+    run_case(f"scale={scale} causal={causal}", 1, 2, 300, 128, "bf16", causal, scale, seed=31)
+
+
+def test_backward_batch_heads_layout():
+    """Several batches and heads in one launch: each head's gradients land in its own slab."""
+    run_case("B=3 H=5", 3, 5, 192, 64, "fp16", True, 0.125, seed=41)
+
+
+# ------------------------------------------------------------ the workloads at full size
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", [
+    ("b1h1n128d64_fp16", [(0, 0)]),
+    ("b4h16n1024d64_fp16", [(0, 0), (3, 15), (2, 7)]),
+    ("b4h16n1024d64_fp16_causal", [(0, 0), (3, 15), (1, 9)]),
+    ("b8h32n2048d128_bf16", [(0, 0), (7, 31)]),
+    ("b2h16n4096d128_bf16_causal", [(0, 0), (1, 15)]),
+    ("b1h32n16384d128_bf16_causal_koff", [(0, 31)]),
+])
+def test_backward_workload(name, heads):
+    """Full-size launch over every head; the listed heads are compared element by
+    element.  O and LSE of the compared heads come from the oracle; the other
+    heads get the HIP forward pass's outputs, which cannot affect the compared
+    heads (heads are independent)."""
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    do = workload_grad_output(w)
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    o, lse = fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    q64, k64, v64 = (to_f64(x) for x in (q, k, v))
+    for b, h in heads:
+        o_h, l_h = oracle_forward_inputs(q64[b, h], k64[b, h], v64[b, h], w.causal, w.scale, w.dtype)
+        o[b, h] = o_h.cuda()
+        lse[b, h] = l_h.cuda()
+    o_r = o.cpu()
+    dq, dk, dv, delta = fa2.backward(qd, kd, vd, o, lse, do.cuda(), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    check_heads(name, q, k, v, o_r, do, (dq, dk, dv, delta), w.causal, w.scale, w.dtype, heads)
+
+
+# ------------------------------------------------------------ properties
+
+def test_backward_deterministic():
+    """No atomics: two calls give bitwise-equal gradients."""
+    q, k, v = make_inputs(2, 4, 1000, 128, "bf16", seed=51)
+    do = make_grad_output(2, 4, 1000, 128, "bf16", seed=51)
+    t = [x.cuda() for x in (q, k, v, do)]
+    o, lse = fa2.forward(t[0], t[1], t[2], causal=True)
+    a = fa2.backward(t[0], t[1], t[2], o, lse, t[3], causal=True)
+    b = fa2.backward(t[0], t[1], t[2], o, lse, t[3], causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_column_sums():
+    """sum_j dK_j = 0 (softmax rows are shift invariant) and sum_j dV_j = sum_i dO_i
+    (rows of P sum to 1): exact identities, checked at a size the oracle is not run at."""
+    B, H, N, d = 1, 4, 4096, 128
+    q, k, v = make_inputs(B, H, N, d, "bf16", seed=61)
+    do = make_grad_output(B, H, N, d, "bf16", seed=61)
+    t = [x.cuda() for x in (q, k, v, do)]
+    o, lse = fa2.forward(t[0], t[1], t[2], causal=False)
+    dq, dk, dv, _ = fa2.backward(t[0], t[1], t[2], o, lse, t[3], causal=False)
+    torch.cuda.synchronize()
+    dk64, dv64, do64 = to_f64(dk), to_f64(dv), to_f64(do)
+    sk = dk64.sum(axis=2)
+    sv = dv64.sum(axis=2) - do64.sum(axis=2)
+    # per-element rounding of dK, dV (u |x|) summed over N rows, plus P's rounding in dV
+    u = UNIT["bf16"]
+    tol_k = 4 * u * np.abs(dk64).sum(axis=2) + 1e-3
+    tol_v = 4 * u * (np.abs(dv64).sum(axis=2) + np.abs(do64).sum(axis=2)) + 1e-3
+    print(f"max|sum dK|={np.abs(sk).max():.3e}, max|sum dV - sum dO|={np.abs(sv).max():.3e}", flush=True)
+    assert np.all(np.abs(sk) <= tol_k)
+    assert np.all(np.abs(sv) <= tol_v)
+
+
+def test_backward_empty_problem():
+    z = torch.empty((0, 2, 64, 64), dtype=torch.float16, device="cuda")
+    lse = torch.empty((0, 2, 64), dtype=torch.float32, device="cuda")
+    dq, dk, dv, delta = fa2.backward(z, z, z, z, lse, z)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and delta.numel() == 0

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward workloads.
+"""Seeded synthetic inputs for the attention workloads (forward and backward).
 
 This module is shared by the tests, the benchmark and the smoke check.  It
 draws random numbers and rounds them to the input dtype; it holds none of the
@@ -12,7 +12,10 @@ Recipe (the same for every workload):
     after V and added to all d entries of K[b, h, j, :];
   * rounding: float32 -> fp16 or bf16, round-to-nearest-even (PyTorch's CPU
     cast).  The GPU and the oracle consume these same rounded tensors; the
-    oracle sees them upcast exactly to float64.
+    oracle sees them upcast exactly to float64;
+  * upstream gradient dO of the backward pass: its own generator,
+    ``default_rng(GRAD_SEED_OFFSET + seed)``, one float32 ``standard_normal``
+    draw of shape [B, H, N, d] (not scaled by sigma), rounded the same way.
 """
 
 from __future__ import annotations
@@ -23,9 +26,13 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "workload_inputs", "to_f64", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_grad_output", "workload_inputs",
+           "workload_grad_output", "to_f64", "torch_dtype"]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+#: dO is drawn from default_rng(GRAD_SEED_OFFSET + seed)
+GRAD_SEED_OFFSET = 1000
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +59,20 @@ class Workload:
         """Counted FLOPs: 4*B*H*N^2*d, halved when causal."""
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Counted backward FLOPs: the five products (S, dP, dV, dK, dQ) of
+        2*N^2*d each, 10*B*H*N^2*d, halved when causal."""
+        f = 10.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def bwd_hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes of the backward pass: Q, K, V, O, dO read once,
+        dQ, dK, dV written once, LSE read and D written and read (fp32)."""
+        rows = self.B * self.H * self.N
+        return 8 * rows * self.d * 2 + 3 * rows * 4
 
     @property
     def hbm_bytes(self) -> int:
@@ -111,6 +132,20 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
         k += c
     td = _DTYPES[dtype]
     return tuple(torch.from_numpy(x).to(td).contiguous() for x in (q, k, v))
+
+
+def make_grad_output(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """The upstream gradient dO [B, H, N, d] of ``dtype`` (CPU, contiguous)."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(_DTYPES)}")
+    rng = np.random.default_rng(GRAD_SEED_OFFSET + seed)
+    g = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    return torch.from_numpy(g).to(_DTYPES[dtype]).contiguous()
+
+
+def workload_grad_output(w: Workload):
+    """The seeded dO of a named workload."""
+    return make_grad_output(w.B, w.H, w.N, w.d, w.dtype, w.seed)
 
 
 def workload_inputs(w: Workload):
