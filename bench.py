@@ -6,10 +6,15 @@ launch) on the headline workload B=8, H=32, N=2048, d=128, bf16, non-causal,
 scale 1/sqrt(d), inputs resident in HBM.  Prints ONE JSON line on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--all] [--copy-calibration BYTES]
+                    [--all] [--copy-calibration BYTES] [--backward]
 
 Throughput is counted as 4*B*H*N^2*d FLOPs per call (halved when causal).
 Timing uses HIP events recorded on the stream the kernel is launched on.
+
+--backward times the backward pass instead (one step = one fa2_bwd call:
+the D, dK/dV and dQ kernels on one stream), counted as 10*B*H*N^2*d FLOPs
+(the five products S, dP, dV, dK, dQ; halved when causal), and prints its
+own JSON line.
 """
 
 from __future__ import annotations
@@ -25,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS (and % of MFMA peak) at N=2048,d=128 bf16"
+BWD_METRIC = "attention bwd TFLOPS (and % of MFMA peak), 10*B*H*N^2*d FLOPs per call"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}   # MI355X dense MFMA peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_fwd_kernel.hpp")
@@ -104,6 +110,92 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
+def cpu_baseline_bwd(w, budget_s: float = 20.0):
+    """The fp64 CPU gradient oracle timed on whole heads of the same workload."""
+    import oracle
+    from workloads import workload_grad_output, workload_inputs, to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = workload_inputs(w)
+    do = workload_grad_output(w)
+    nh = w.B * w.H
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < nh:
+        b, h = divmod(heads, w.H)
+        oracle.attention_backward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), to_f64(do[b, h]),
+                                  w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(heads * (w.bwd_flops / nh) / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, fp64 NumPy gradient "
+                      f"oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
+
+
+def run_backward(w, steps, warmup):
+    import torch
+    import exact_attention_63_amd as fa2
+    from workloads import workload_grad_output, workload_inputs
+    q, k, v = (t.cuda() for t in workload_inputs(w))
+    do = workload_grad_output(w).cuda()
+    o, lse = fa2.forward(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+
+    def step():
+        fa2.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
+    return time_gpu(step, steps, warmup)
+
+
+def backward_main(args, w):
+    ms, wall_ms = run_backward(w, args.steps, args.warmup)
+    peak = PEAK_TFLOPS[w.dtype]
+    tflops = w.bwd_flops / (ms * 1e-3) / 1e12
+    if args.all:
+        from workloads import WORKLOADS
+        print(f"{'workload (backward)':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}", file=sys.stderr)
+        for other in WORKLOADS.values():
+            oms, _ = run_backward(other, max(5, args.steps // 2), max(2, args.warmup // 2))
+            t = other.bwd_flops / (oms * 1e-3) / 1e12
+            print(f"{other.name:36s} {oms:9.4f} {t:9.1f} {100 * t / PEAK_TFLOPS[other.dtype]:6.1f}%",
+                  file=sys.stderr, flush=True)
+    line = {
+        "metric": BWD_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and dO, rounded to the dtype)",
+        "config": {**w.describe(), "pass": "backward (D, dK/dV, dQ kernels)", "parallelism": "single GPU",
+                   "wall_ms_per_step": round(wall_ms, 5)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": None,
+            "scope": "the whole call (three kernels); per-kernel durations in the rocprofv3 summary",
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(w)
+    print(json.dumps(line), flush=True)
+
+
 def run_workload(w, steps, warmup, variant=0):
     import torch
     import exact_attention_63_amd as fa2
@@ -141,6 +233,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -159,6 +252,9 @@ def main():
     from workloads import HEADLINE, WORKLOADS
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
+    if args.backward:
+        backward_main(args, w)
+        return
     ms, wall_ms = run_workload(w, args.steps, args.warmup, args.variant)
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
