@@ -138,7 +138,7 @@ def cpu_baseline_bwd(w, budget_s: float = 20.0):
                       f"oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
-def run_backward(w, steps, warmup):
+def run_backward(w, steps, warmup, variant=0):
     import torch
     import exact_attention_63_amd as fa2
     from workloads import workload_grad_output, workload_inputs
@@ -149,20 +149,21 @@ def run_backward(w, steps, warmup):
     delta = torch.empty_like(lse)
 
     def step():
-        fa2.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+        fa2.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, variant=variant, dq=dq, dk=dk, dv=dv,
+                     delta=delta)
 
     return time_gpu(step, steps, warmup)
 
 
 def backward_main(args, w):
-    ms, wall_ms = run_backward(w, args.steps, args.warmup)
+    ms, wall_ms = run_backward(w, args.steps, args.warmup, args.variant)
     peak = PEAK_TFLOPS[w.dtype]
     tflops = w.bwd_flops / (ms * 1e-3) / 1e12
     if args.all:
         from workloads import WORKLOADS
         print(f"{'workload (backward)':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}", file=sys.stderr)
         for other in WORKLOADS.values():
-            oms, _ = run_backward(other, max(5, args.steps // 2), max(2, args.warmup // 2))
+            oms, _ = run_backward(other, max(5, args.steps // 2), max(2, args.warmup // 2), args.variant)
             t = other.bwd_flops / (oms * 1e-3) / 1e12
             print(f"{other.name:36s} {oms:9.4f} {t:9.1f} {100 * t / PEAK_TFLOPS[other.dtype]:6.1f}%",
                   file=sys.stderr, flush=True)
@@ -179,7 +180,8 @@ def backward_main(args, w):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and dO, rounded to the dtype)",
-        "config": {**w.describe(), "pass": "backward (D, dK/dV, dQ kernels)", "parallelism": "single GPU",
+        "config": {**w.describe(), "pass": "backward (D, dK/dV, dQ kernels)", "variant": args.variant,
+                   "parallelism": "single GPU",
                    "wall_ms_per_step": round(wall_ms, 5)},
         "roofline": {
             "bound": "mfma",
@@ -229,7 +231,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--variant", type=int, default=0, help="tile variant (0 = tuned default)")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="tile variant of the timed pass (0 = tuned default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")

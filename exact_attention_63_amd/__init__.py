@@ -17,7 +17,7 @@ import math
 import os
 
 __all__ = [
-    "forward", "backward", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "forward", "backward", "bwd_num_variants", "bwd_variant_name", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
     "default_variant",
     "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
     "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
@@ -54,6 +54,9 @@ EXPORTS = {
     "fa2_bwd_fp16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
     "fa2_bwd_bf16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
     "fa2_bwd_check": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _I]),
+    "fa2_bwd_variant": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P, _I, _I]),
+    "fa2_bwd_num_variants": (_I, []),
+    "fa2_bwd_variant_name": (ctypes.c_char_p, [_I]),
     "fa2_default_variant": (_I, [_I, _I, _I]),
     "fa2_num_variants": (_I, []),
     "fa2_variant_name": (ctypes.c_char_p, [_I]),
@@ -171,8 +174,17 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
     return out, lse
 
 
+def bwd_num_variants() -> int:
+    return lib().fa2_bwd_num_variants()
+
+
+def bwd_variant_name(variant: int) -> str | None:
+    s = lib().fa2_bwd_variant_name(variant)
+    return None if s is None else s.decode()
+
+
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, *,
-             dq=None, dk=None, dv=None, delta=None):
+             variant: int = 0, dq=None, dk=None, dv=None, delta=None):
     """Attention backward: returns (dQ, dK, dV in q's dtype, delta [B,H,N] float32).
 
     q, k, v, o, do: contiguous CUDA tensors [B, H, N, d] of one dtype (fp16 or
@@ -180,7 +192,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     outputs for q, k, v with the same causal flag and scale (default
     1/sqrt(d)).  delta receives rowsum(dO * O).  The three kernels are
     enqueued on the current stream of q's device; the call does not
-    synchronise.  dq, dk, dv, delta may pass preallocated outputs.
+    synchronise.  dq, dk, dv, delta may pass preallocated outputs.  variant
+    selects the dK/dV kernel configuration (0 = default, see
+    ``bwd_variant_name``).
     """
     import torch
     if q.dim() != 4:
@@ -216,9 +230,10 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
         raise ValueError("delta must be a contiguous float32 tensor [B, H, N] on q's device")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        rc = lib().fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                           B, H, N, d, int(bool(causal)), float(scale), stream, code)
+        rc = lib().fa2_bwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   delta.data_ptr(), B, H, N, d, int(bool(causal)), float(scale), stream,
+                                   code, int(variant))
     if rc != FA2_OK:
-        raise Fa2Error(rc, "fa2_bwd")
+        raise Fa2Error(rc, "fa2_bwd_variant")
     return dq, dk, dv, delta

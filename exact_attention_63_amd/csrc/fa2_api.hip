@@ -176,9 +176,15 @@ typedef void (*delta_fn)(BwdArgs, long long);
 using KvTile = BwdTile<4, 1>;
 using QTile = BwdTile<8, 2>;
 
+// dK/dV alternative: 8 waves (128 keys), two per SIMD, the dV and dK
+// products split between the two waves of a SIMD.
+constexpr int kSplitKeys = 128;
+
 struct BwdKernels {
   delta_fn delta[2][2];        // [bf16][d == 128]
   bwd_fn dkdv[2][2][2];        // [bf16][d == 128][causal]
+  bwd_fn dkdv_split[2][2][2];
+  bwd_fn dkdv_ring[2][2][2];
   bwd_fn dq[2][2][2];
 };
 
@@ -187,6 +193,10 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.delta[BF16][D == 128] = fa2::fa2_bwd_delta_kernel<BF16, D>;
   t.dkdv[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_kernel<BF16, D, false, KvTile>;
   t.dkdv[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_kernel<BF16, D, true, KvTile>;
+  t.dkdv_split[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, false>;
+  t.dkdv_split[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, false>;
+  t.dkdv_ring[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true>;
+  t.dkdv_ring[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
 }
@@ -202,10 +212,27 @@ BwdKernels make_bwd_kernels() {
 
 const BwdKernels kBwd = make_bwd_kernels();
 
+// backward variants: 0 = default, 1 = one-wave-per-SIMD dK/dV kernel,
+// 2 = role-split dK/dV kernel, 3 = role-split with a 4-stage direct-copy
+// ring (the dQ and D kernels are the same in all)
+constexpr int kNumBwdVariants = 4;
+const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
+                                                       "dkdv_w8_split_occ2_ring4"};
+
+// Measured on MI355X (bench.py --backward, alternating runs on one box): at
+// d = 128 the role-split kernel on the direct-copy ring is fastest (headline
+// shape 2.57 against 2.95 ms per call, N = 16384 causal 10.8 against 12.1 ms);
+// at d = 64 the one-wave-per-SIMD kernel (0.13 against 0.14 ms).
+int default_bwd_variant(int d, int causal) {
+  (void)causal;
+  return d == 128 ? 3 : 1;
+}
+
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
               const void* dout, const void* dq, const void* dk, const void* dv, const void* delta,
-              int B, int H, int N, int d, int causal, float scale, int dtype) {
+              int B, int H, int N, int d, int causal, float scale, int dtype, int variant) {
   if (dtype != FA2_DTYPE_FP16 && dtype != FA2_DTYPE_BF16) return FA2_ERR_ARG;
+  if (variant < 0 || variant >= kNumBwdVariants) return FA2_ERR_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_ARG;
   if (!finite_bits(scale)) return FA2_ERR_ARG;
   if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
@@ -240,8 +267,8 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
             const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
-            int causal, float scale, hipStream_t stream, int dtype) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype);
+            int causal, float scale, hipStream_t stream, int dtype, int variant) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, variant);
   if (st == kEmpty) return FA2_OK;
   if (st != FA2_OK) return st;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
@@ -271,9 +298,16 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
-  a.nblk = (N + KvTile::BR - 1) / KvTile::BR;
-  hipLaunchKernelGGL(kBwd.dkdv[bf16][big][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
-                     dim3(KvTile::THREADS), 0, stream, a);
+  const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
+  if (vi == 2 || vi == 3) {
+    a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
+    bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal] : kBwd.dkdv_ring[bf16][big][causal];
+    hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
+  } else {
+    a.nblk = (N + KvTile::BR - 1) / KvTile::BR;
+    hipLaunchKernelGGL(kBwd.dkdv[bf16][big][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
+                       dim3(KvTile::THREADS), 0, stream, a);
+  }
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   a.nblk = (N + QTile::BR - 1) / QTile::BR;
@@ -319,7 +353,22 @@ FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const 
 FA2_EXPORT int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
                        int N, int d, int causal, float scale, hipStream_t stream, int dtype) {
-  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype);
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype, 0);
+}
+
+FA2_EXPORT int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               float* delta, int B, int H, int N, int d, int causal, float scale,
+                               hipStream_t stream, int dtype, int variant) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream, dtype,
+                 variant);
+}
+
+FA2_EXPORT int fa2_bwd_num_variants(void) { return kNumBwdVariants; }
+
+FA2_EXPORT const char* fa2_bwd_variant_name(int variant) {
+  if (variant < 0 || variant >= kNumBwdVariants) return nullptr;
+  return kBwdVariantNames[variant];
 }
 
 FA2_EXPORT int fa2_bwd_fp16(const void* q, const void* k, const void* v, const void* o,
@@ -327,7 +376,7 @@ FA2_EXPORT int fa2_bwd_fp16(const void* q, const void* k, const void* v, const v
                             float* delta, int B, int H, int N, int d, int causal, float scale,
                             hipStream_t stream) {
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream,
-                 FA2_DTYPE_FP16);
+                 FA2_DTYPE_FP16, 0);
 }
 
 FA2_EXPORT int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
@@ -335,14 +384,14 @@ FA2_EXPORT int fa2_bwd_bf16(const void* q, const void* k, const void* v, const v
                             float* delta, int B, int H, int N, int d, int causal, float scale,
                             hipStream_t stream) {
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream,
-                 FA2_DTYPE_BF16);
+                 FA2_DTYPE_BF16, 0);
 }
 
 FA2_EXPORT int fa2_bwd_check(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const void* dq, const void* dk,
                              const void* dv, const float* delta, int B, int H, int N, int d,
                              int causal, float scale, int dtype) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype);
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, 0);
   return st == kEmpty ? FA2_OK : st;
 }
 

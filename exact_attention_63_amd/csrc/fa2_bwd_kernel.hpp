@@ -124,6 +124,18 @@ __global__ __launch_bounds__(256) void fa2_bwd_delta_kernel(BwdArgs a, long long
   if (row < rows && ch == 0) a.delta[row] = acc;
 }
 
+// 4 bytes per lane from a buffer straight into LDS (lane l writes lds + 4*l),
+// as inline assembly like lds_dma16_asm: invisible to the compiler's wait
+// counting, so the kernel's own s_waitcnt vmcnt and barriers order it.
+__device__ __forceinline__ void lds_dma4_asm(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(r)
+               : "memory", "m0");
+}
+
 // LDS byte offsets of a lane's operand fragments in an unpadded, swizzled
 // [row][D] tile (see chunk_swizzle):
 //   frag_base: 16-byte read of row (lane % 32), chunk 2*dk + lane/32, for the
@@ -377,6 +389,281 @@ void fa2_bwd_dkdv_kernel(BwdArgs a) {
       wv[1] = E::pack(dva[db][4 * i + 2], dva[db][4 * i + 3]);
       __builtin_amdgcn_raw_buffer_store_b64(wk, dkr, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64(wv, dvr, off, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with the two products split between the two waves of a SIMD: one
+// workgroup per (key block of 128 keys, head), 8 waves, two per SIMD.  Wave w
+// owns keys [k_wg + 32*(w%4), +32); waves 0-3 accumulate dV^T = dO^T P and
+// waves 4-7 dK^T = Q^T dS for the same keys, so each wave holds one
+// accumulator (and the dV waves no V rows) and two waves fit in a SIMD's
+// registers.  Both recompute S = Q K_w^T (the price of the split: 10 instead
+// of 8 N^2 d MFMA FLOPs per head); only the dK waves compute dP.  Query tiles
+// of 32 rows (Q, dO, LSE in base 2, D) are staged in LDS, two stages.
+//
+// RING = false: register-staged copies, one tile ahead, two LDS stages.
+// RING = true: Q, dO, LSE and D go straight from HBM into a 4-stage LDS ring
+// (buffer_load ... lds issued as inline assembly, no staging registers),
+// three tiles ahead; each wave waits for its own copies of a tile, then one
+// barrier per tile publishes it and frees the stage of the previous tile.
+// The compiler does not see the copies (with the builtin it cannot tell the
+// ring's stages apart and drains every copy in flight before each barrier).  LSE then stays in base e in LDS
+// and is scaled by log2(e) when read.
+template <bool BF16, int D, bool CAUSAL, bool RING>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
+  using E = Elem<BF16>;
+  constexpr int T = 512, BK = 128;
+  constexpr int BQ = 32;                    // queries per tile
+  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
+  constexpr int TSZ = BQ * KROW;            // bytes of one Q (or dO) tile
+  // ring stages hold 64 LSE and 64 D slots (a 4-byte copy instruction fills 64)
+  constexpr int STAGE = 2 * TSZ + (RING ? 2 * 64 * 4 : 2 * BQ * 4);
+  constexpr int NS = RING ? 4 : 2;
+  constexpr int CH = BQ * D / 8;            // 16-byte chunks per tile: 512 (d = 128) or 256 (d = 64)
+  static_assert(CH <= T, "one chunk per thread and tensor");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int grp = wave & 3;                 // key group
+  // waves 4-7: dK; waves 0-3: dV (read from lane 0: the role is wave-uniform)
+  const bool dk_role = __builtin_amdgcn_readfirstlane(wave) >= 4;
+
+  int bh, kblk;
+  {
+    const int i = blockIdx.x;
+    const int total = a.nblk * a.BH;
+    if constexpr (!CAUSAL) {
+      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+      bh = logical / a.nblk;
+      kblk = logical % a.nblk;
+    } else {
+      bh = i % a.BH;
+      kblk = i / a.BH;
+    }
+  }
+  const int N = a.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  auto rsrc = [&](const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
+  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+
+  const int k_wg = kblk * BK;
+  const int k_w = k_wg + 32 * grp;
+  const int key = k_w + lr;
+
+  // K rows (both roles) and V rows (dK role) of the group's keys: B operands
+  u32x4 kf[DK], vf[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    const uint32_t off = (uint32_t)(key * KROW + (2 * dk + lh) * 16);
+    kf[dk] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+    vf[dk] = dk_role ? __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0) : u32x4{};
+  }
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const int nt = (N + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? k_wg / BQ : 0;
+
+  u32x4 qst{}, dost{};
+  float lst = 0.f;
+  const int crow = tid / (D / 8), cch = tid % (D / 8);   // the chunk this thread copies
+  auto load = [&](int q0) {
+    if (tid < CH) {
+      const uint32_t off = (uint32_t)((q0 + crow) * KROW + cch * 16);
+      qst = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
+      dost = __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0);
+    }
+    if (tid >= T - 2 * BQ) {
+      const int r = tid - (T - 2 * BQ);
+      lst = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           r < BQ ? lser : dlr, (uint32_t)((q0 + (r % BQ)) * 4), 0, 0));
+    }
+  };
+  auto store = [&](int stg) {
+    uint8_t* base = smem + stg * STAGE;
+    if (tid < CH) {
+      const int off = crow * KROW + 16 * (cch ^ chunk_swizzle<D>(crow));
+      *(u32x4*)(base + off) = qst;
+      *(u32x4*)(base + TSZ + off) = dost;
+    }
+    if (tid >= T - 2 * BQ) {
+      const int r = tid - (T - 2 * BQ);
+      ((float*)(base + 2 * TSZ))[r] = r < BQ ? lst * kLog2e : lst;
+    }
+  };
+
+  const FragAddr<D> fa(lane);
+  const float c = a.c;
+
+  // one 32-query tile: S (and dP), then P or dS, then one product
+  auto compute = [&](const uint8_t* st, int q0, bool masked, auto role_tag) {
+    constexpr bool DKR = decltype(role_tag)::value;
+    const uint8_t* qt = st;
+    const uint8_t* dot = st + TSZ;
+    const float* l2 = (const float*)(st + 2 * TSZ);
+    const float* dl = l2 + (RING ? 64 : BQ);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      s = E::mfma(fa.fread(qt, 0, dk), kf[dk], s);
+      if constexpr (DKR) dp = E::mfma(fa.fread(dot, 0, dk), vf[dk], dp);
+    }
+    u32x4 pk[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 lq = *(const f32x4*)(l2 + 8 * g + 4 * lh);
+      if constexpr (RING) lq *= kLog2e;
+      f32x4 dq4 = f32x4{};
+      if constexpr (DKR) dq4 = *(const f32x4*)(dl + 8 * g + 4 * lh);
+      float val[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = 4 * g + b;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq[b]));
+        if (masked) {
+          const int q = q0 + 8 * g + 4 * lh + b;
+          const bool vis = q < N && (!CAUSAL || key <= q);
+          pv = vis ? pv : 0.f;
+        }
+        val[b] = DKR ? pv * (dp[r] - dq4[b]) : pv;
+      }
+      pk[g >> 1][2 * (g & 1)] = E::pack(val[0], val[1]);
+      pk[g >> 1][2 * (g & 1) + 1] = E::pack(val[2], val[3]);
+    }
+    // dV^T += dO^T P  or  dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(DKR ? qt : dot, 16 * h, db), pk[h], acc[db]);
+  };
+
+  auto tile = [&](const uint8_t* st, int t) {
+    const int q0 = t * BQ;
+    const bool skip = CAUSAL && q0 + BQ - 1 < k_w;
+    if (!skip) {
+      const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < k_w + 31);
+      if (dk_role) compute(st, q0, masked, std::true_type{});
+      else compute(st, q0, masked, std::false_type{});
+    }
+  };
+
+  if constexpr (!RING) {
+    if (t0 < nt) {
+      load(t0 * BQ);
+      store(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      for (int t = t0; t < nt; ++t) {
+        const int stg = (t - t0) & 1;
+        if (t + 1 < nt) load((t + 1) * BQ);
+        tile(smem + stg * STAGE, t);
+        if (t + 1 < nt) store(stg ^ 1);
+        __syncthreads();
+      }
+    }
+  } else {
+    // Copy instructions of one tile: NI per tensor (Q, dO) of 1 KiB each, two
+    // per wave for d = 128 and one for d = 64; waves 0 and 1 also copy the 64
+    // LSE and D slots (4 bytes per lane; slots past the tile are not read).
+    constexpr int NI = TSZ / 1024;
+    constexpr int IPW = 2 * NI / 8;
+    static_assert(2 * NI % 8 == 0 && IPW >= 1, "tile copies must split evenly over the waves");
+    // the wave index read from lane 0, so that the copy's buffer descriptor
+    // and LDS destination (scalar operands) are known to be wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t dsrc[IPW];
+    int ddst[IPW];
+    bool dq_t[IPW];
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) {
+      const int i = wv * IPW + k;                 // copy instruction index
+      dq_t[k] = i >= NI;                          // false: Q, true: dO
+      const int b = (i % NI) * 1024 + 16 * lane;  // byte of the tile this lane fills
+      const int row = b / KROW, phys = (b % KROW) / 16;
+      dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+      ddst[k] = (dq_t[k] ? TSZ : 0) + (i % NI) * 1024;
+    }
+    const bool stat_wave = wv < 2;                // wave 0: LSE, wave 1: D
+    // Tile offsets go into the per-lane (VGPR) offset: the buffer range check
+    // covers it (not the SGPR offset), so rows past N read as zero.
+    auto dma = [&](int t, int stg) {
+      uint8_t* base = smem + stg * STAGE;
+      const uint32_t qoff = (uint32_t)(t * BQ * KROW);
+#pragma unroll
+      for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k] + qoff, 0);
+      if (stat_wave)
+        lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * (t * BQ + lane)));
+    };
+    // copies this wave issues per tile
+    auto wait_tile = [&](bool next_in_flight, bool next2_in_flight) {
+      // tiles issued after the one awaited: up to two (tiles t+1, t+2)
+      const int after = (next_in_flight ? 1 : 0) + (next2_in_flight ? 1 : 0);
+      if (stat_wave) {
+        if (after == 2) FA2_WAIT_VMCNT(2 * (IPW + 1));
+        else if (after == 1) FA2_WAIT_VMCNT(IPW + 1);
+        else FA2_WAIT_VMCNT(0);
+      } else {
+        if (after == 2) FA2_WAIT_VMCNT(2 * IPW);
+        else if (after == 1) FA2_WAIT_VMCNT(IPW);
+        else FA2_WAIT_VMCNT(0);
+      }
+    };
+    if (t0 < nt) {
+      // K, V fragments were loaded first; then tiles t0 .. t0+2
+      const int first = nt - t0 < 3 ? nt - t0 : 3;
+      for (int i = 0; i < first; ++i) dma(t0 + i, i);
+      // The fragment loads are older than every copy: they have landed once
+      // at most this wave's copies remain.  Passing the fragment registers
+      // through an empty statement here puts the compiler's own wait for
+      // them before the loop rather than inside it, where it would also
+      // drain the copies of the next tiles on every iteration.
+      const int per_tile = IPW + (stat_wave ? 1 : 0);
+      if (first * per_tile >= 3 * (IPW + 1)) FA2_WAIT_VMCNT(3 * (IPW + 1));
+      else if (first * per_tile >= 3 * IPW) FA2_WAIT_VMCNT(3 * IPW);
+      else if (first * per_tile >= 2 * (IPW + 1)) FA2_WAIT_VMCNT(2 * (IPW + 1));
+      else if (first * per_tile >= 2 * IPW) FA2_WAIT_VMCNT(2 * IPW);
+      else if (first * per_tile >= IPW + 1) FA2_WAIT_VMCNT(IPW + 1);
+      else if (first * per_tile >= IPW) FA2_WAIT_VMCNT(IPW);
+      else FA2_WAIT_VMCNT(0);
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(kf[dk]), "v"(vf[dk]));
+      for (int t = t0; t < nt; ++t) {
+        const int i = t - t0;
+        wait_tile(t + 1 < nt, t + 2 < nt);
+        // every wave's copies of tile t have landed and every wave is done
+        // with tile t-1, whose stage (i+3)%4 now receives tile t+3
+        __syncthreads();
+        if (t + 3 < nt) dma(t + 3, (i + 3) & 3);
+        tile(smem + (i & 3) * STAGE, t);
+      }
+    }
+  }
+
+  // ---- epilogue: dV = dV^T or dK = scale * dK^T, transposed back ----------
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)(dk_role ? a.dk : a.dv) + head_off), 0, head_bytes, kBufferWord3);
+  const float sc = dk_role ? a.scale : 1.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * lh;
+      u32x2 w;
+      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
+      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
+      __builtin_amdgcn_raw_buffer_store_b64(w, outr, (uint32_t)(key * KROW + d * 2), 0, 0);
     }
   }
 }

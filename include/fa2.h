@@ -164,6 +164,32 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
                  int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * fa2_bwd_variant -- fa2_bwd with an explicit kernel configuration for the
+ * dK/dV step, for tuning and for tests that every configuration computes the
+ * same gradients.  variant 0 is the default that fa2_bwd uses; the others are
+ * described by fa2_bwd_variant_name():
+ *   1 "dkdv_w4_occ1": 4 waves x 32 keys per workgroup, one wave per SIMD,
+ *     each wave accumulating both dK and dV of its keys;
+ *   2 "dkdv_w8_split_occ2": 8 waves, two per SIMD, the two waves of a SIMD
+ *     own the same 32 keys, one accumulating dV and the other dK (both
+ *     recompute S = Q K^T);
+ *   3 "dkdv_w8_split_occ2_ring4": variant 2 with its query tiles copied
+ *     straight from memory into a 4-stage LDS ring, three tiles ahead.
+ * The default is variant 3 for d = 128 and variant 1 for d = 64.
+ * Returns FA2_ERR_ARG for an unknown variant.
+ */
+int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* delta,
+                    int B, int H, int N, int d, int causal, float scale, hipStream_t stream,
+                    int dtype, int variant);
+
+/* Number of backward variants (including the default, 0). */
+int fa2_bwd_num_variants(void);
+
+/* Static name of a backward variant ("default" for 0), or NULL when out of range. */
+const char* fa2_bwd_variant_name(int variant);
+
+/*
  * fa2_bwd_check -- run exactly the argument validation of fa2_bwd and return
  * its status, without launching anything or calling the HIP runtime.
  */

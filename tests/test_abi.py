@@ -35,7 +35,8 @@ def test_header_declares_the_named_call():
     names = declared_functions()
     for n in ["fa2_fwd", "fa2_fwd_fp16", "fa2_fwd_bf16", "fa2_fwd_variant", "fa2_fwd_check",
               "fa2_status_string", "fa2_version", "fa2_num_variants", "fa2_variant_name",
-              "fa2_default_variant", "fa2_bwd", "fa2_bwd_fp16", "fa2_bwd_bf16", "fa2_bwd_check"]:
+              "fa2_default_variant", "fa2_bwd", "fa2_bwd_fp16", "fa2_bwd_bf16", "fa2_bwd_check",
+              "fa2_bwd_variant", "fa2_bwd_num_variants", "fa2_bwd_variant_name"]:
         assert n in names
 
 
@@ -203,6 +204,14 @@ def test_bwd_adjacent_outputs_do_not_alias(lib):
     tbytes = B * H * N * d * 2
     assert bchk(dq=DQ, dk=DQ + tbytes, dv=DQ + 2 * tbytes) == fa2.FA2_OK
     assert bchk(dq=DQ, dk=DQ + tbytes - 16) == fa2.FA2_ERR_ALIAS
+
+
+def test_bwd_variant_names(lib):
+    n = fa2.bwd_num_variants()
+    assert n >= 2
+    assert fa2.bwd_variant_name(0) == "default"
+    assert all(fa2.bwd_variant_name(i) for i in range(n))
+    assert fa2.bwd_variant_name(n) is None and fa2.bwd_variant_name(-1) is None
 
 
 def test_python_backward_rejects_cpu_tensors(lib):

@@ -81,9 +81,9 @@ def compare(name, got, ref, bound):
     assert ratio <= 1.0, f"{name}: error above the derived bound (worst err/tol {ratio:.3f})"
 
 
-def gpu_backward(q, k, v, o, lse, do, causal, scale):
+def gpu_backward(q, k, v, o, lse, do, causal, scale, variant=0):
     t = [x.cuda() for x in (q, k, v, o, lse, do)]
-    dq, dk, dv, delta = fa2.backward(*t, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa2.backward(*t, causal=causal, scale=scale, variant=variant)
     torch.cuda.synchronize()
     return dq, dk, dv, delta
 
@@ -100,12 +100,13 @@ def check_heads(what, q, k, v, o_r, do, out, causal, scale, dtype, heads):
             compare(name, gi[b, h], ri, bi)
 
 
-def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0, key_offset=None):
+def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0, key_offset=None,
+             variant=0):
     q, k, v = make_inputs(B, H, N, d, dtype, seed, sigma, key_offset)
     do = make_grad_output(B, H, N, d, dtype, seed)
     q64, k64, v64 = (to_f64(x) for x in (q, k, v))
     o_r, lse = oracle_forward_inputs(q64, k64, v64, causal, scale, dtype)
-    out = gpu_backward(q, k, v, o_r, lse, do, causal, scale)
+    out = gpu_backward(q, k, v, o_r, lse, do, causal, scale, variant)
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(H)]
     check_heads(what, q, k, v, o_r, do, out, causal, scale, dtype, heads)
@@ -117,22 +118,28 @@ def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 31, 64, 65, 127, 129, 200, 513])
-def test_backward_edge_shapes(N, d, causal, dtype):
-    """Ragged N (partial query and key tiles, partial workgroups), single rows."""
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_backward_edge_shapes(variant, N, d, causal, dtype):
+    """Ragged N (partial query and key tiles, partial workgroups), single rows,
+    for every dK/dV configuration."""
     seed = 20_000 + N * 8 + (d == 128) * 4 + causal * 2 + (dtype == "bf16")
-    run_case(f"N={N} d={d} causal={causal} {dtype}", 1, 2, N, d, dtype, causal, 1.0 / math.sqrt(d), seed)
+    run_case(f"v{variant} N={N} d={d} causal={causal} {dtype}", 1, 2, N, d, dtype, causal, 1.0 / math.sqrt(d),
+             seed, variant=variant)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_scales(scale, causal):
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_backward_scales(variant, scale, causal):
     """Zero and negative scales (P uniform over the visible keys; sign flips)."""
-    run_case(f"scale={scale} causal={causal}", 1, 2, 300, 128, "bf16", causal, scale, seed=31)
+    run_case(f"v{variant} scale={scale} causal={causal}", 1, 2, 300, 128, "bf16", causal, scale, seed=31,
+             variant=variant)
 
 
-def test_backward_batch_heads_layout():
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_backward_batch_heads_layout(variant):
     """Several batches and heads in one launch: each head's gradients land in its own slab."""
-    run_case("B=3 H=5", 3, 5, 192, 64, "fp16", True, 0.125, seed=41)
+    run_case(f"v{variant} B=3 H=5", 3, 5, 192, 64, "fp16", True, 0.125, seed=41, variant=variant)
 
 
 # ------------------------------------------------------------ the workloads at full size
