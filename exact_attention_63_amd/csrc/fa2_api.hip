@@ -186,6 +186,7 @@ struct BwdKernels {
   bwd_fn dkdv_split[2][2][2];
   bwd_fn dkdv_ring[2][2][2];
   bwd_fn dq[2][2][2];
+  bwd_fn dq_ring[2][2][2];
 };
 
 template <bool BF16, int D>
@@ -199,6 +200,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_ring[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
+  t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
+  t.dq_ring[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, true>;
 }
 
 BwdKernels make_bwd_kernels() {
@@ -214,10 +217,13 @@ const BwdKernels kBwd = make_bwd_kernels();
 
 // backward variants: 0 = default, 1 = one-wave-per-SIMD dK/dV kernel,
 // 2 = role-split dK/dV kernel, 3 = role-split with a 4-stage direct-copy
-// ring (the dQ and D kernels are the same in all)
-constexpr int kNumBwdVariants = 4;
+// ring; 4 and 5 = variants 3 and 1 with the dQ kernel on a 3-stage
+// direct-copy ring (1-3 use the register-staged dQ kernel)
+constexpr int kNumBwdVariants = 6;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
-                                                       "dkdv_w8_split_occ2_ring4"};
+                                                       "dkdv_w8_split_occ2_ring4",
+                                                       "dkdv_w8_split_occ2_ring4_dq_ring3",
+                                                       "dkdv_w4_occ1_dq_ring3"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the role-split kernel on the direct-copy ring is fastest (headline
@@ -299,7 +305,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  if (vi == 2 || vi == 3) {
+  if (vi == 2 || vi == 3 || vi == 4) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal] : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
@@ -311,8 +317,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   a.nblk = (N + QTile::BR - 1) / QTile::BR;
-  hipLaunchKernelGGL(kBwd.dq[bf16][big][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
-                     dim3(QTile::THREADS), 0, stream, a);
+  bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal] : kBwd.dq[bf16][big][causal];
+  hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }

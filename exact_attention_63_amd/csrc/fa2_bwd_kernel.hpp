@@ -127,12 +127,13 @@ __global__ __launch_bounds__(256) void fa2_bwd_delta_kernel(BwdArgs a, long long
 // 4 bytes per lane from a buffer straight into LDS (lane l writes lds + 4*l),
 // as inline assembly like lds_dma16_asm: invisible to the compiler's wait
 // counting, so the kernel's own s_waitcnt vmcnt and barriers order it.
-__device__ __forceinline__ void lds_dma4_asm(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset) {
+__device__ __forceinline__ void lds_dma4_asm(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voffset,
+                                             int soffset) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(dst), "v"(voffset), "s"(r)
+               : "s"(dst), "v"(voffset), "s"(r), "s"(soffset)
                : "memory", "m0");
 }
 
@@ -596,15 +597,15 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
       ddst[k] = (dq_t[k] ? TSZ : 0) + (i % NI) * 1024;
     }
     const bool stat_wave = wv < 2;                // wave 0: LSE, wave 1: D
-    // Tile offsets go into the per-lane (VGPR) offset: the buffer range check
-    // covers it (not the SGPR offset), so rows past N read as zero.
+    // The tile's offset is the copy's SGPR offset; the buffer range check
+    // covers the SGPR, VGPR and instruction offsets together (measured on
+    // gfx950), so rows past N read as zero.
     auto dma = [&](int t, int stg) {
       uint8_t* base = smem + stg * STAGE;
-      const uint32_t qoff = (uint32_t)(t * BQ * KROW);
+      const int qoff = t * BQ * KROW;
 #pragma unroll
-      for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k] + qoff, 0);
-      if (stat_wave)
-        lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * (t * BQ + lane)));
+      for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k], qoff);
+      if (stat_wave) lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * lane), t * BQ * 4);
     };
     // copies this wave issues per tile
     auto wait_tile = [&](bool next_in_flight, bool next2_in_flight) {
@@ -671,22 +672,25 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (query block of 32*NW queries, head), wave w owns
 // queries [q_wg + 32w, +32).  Key tiles of 64 rows: K and V (row-major,
-// swizzled) staged in LDS, two stages, register-staged copies.
-template <bool BF16, int D, bool CAUSAL, class TL>
+// swizzled) staged in LDS.  RING = false: two stages, register-staged copies
+// one tile ahead; RING = true: three stages filled straight from memory by
+// inline-assembly copies two tiles ahead (as in the dK/dV ring).
+template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(TL::THREADS, TL::THREADS),
                           amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void fa2_bwd_dq_kernel(BwdArgs a) {
   using E = Elem<BF16>;
-  constexpr int T = TL::THREADS, BR = TL::BR;
+  constexpr int T = TL::THREADS, BR = TL::BR, NW = TL::NW;
   constexpr int BC = 64;                    // keys per tile
   constexpr int NKB = BC / 32;
   constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
   constexpr int TSZ = BC * KROW;
   constexpr int STAGE = 2 * TSZ;
+  constexpr int NS = RING ? 3 : 2;
   constexpr int CH = BC * D / 8;
-  constexpr int CH_T = CH / T;
-  static_assert(CH % T == 0, "tile copy must split evenly over threads");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int CH_T = RING ? 1 : CH / T;
+  static_assert(RING || CH % T == 0, "tile copy must split evenly over threads");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
@@ -817,20 +821,71 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
         for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(kt, 32 * kb + 16 * h, db), dsp[kb][h], acc[db]);
   };
 
-  load(0);
-  store(0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
+  auto tile = [&](const uint8_t* st, int j) {
     const int key0 = j * BC;
-    if (j + 1 < nt) load(key0 + BC);
     const bool skip = CAUSAL && key0 > q_w + 31;   // tile entirely above this wave's diagonal
     if (!skip) {
       const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
-      compute(smem + (j & 1) * STAGE, key0, masked);
+      compute(st, key0, masked);
     }
-    if (j + 1 < nt) store((j + 1) & 1);
+  };
+
+  if constexpr (!RING) {
+    load(0);
+    store(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    for (int j = 0; j < nt; ++j) {
+      if (j + 1 < nt) load((j + 1) * BC);
+      tile(smem + (j & 1) * STAGE, j);
+      if (j + 1 < nt) store((j + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // NI copy instructions of 1 KiB per tensor and tile, IPW per wave
+    constexpr int NI = TSZ / 1024;
+    constexpr int IPW = 2 * NI / NW;
+    static_assert(2 * NI % NW == 0 && IPW >= 1 && IPW <= 7, "tile copies must split evenly over the waves");
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t dsrc[IPW];
+    int ddst[IPW];
+    bool isv[IPW];
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) {
+      const int i = wv * IPW + k;
+      isv[k] = i >= NI;                           // false: K, true: V
+      const int b = (i % NI) * 1024 + 16 * lane;
+      const int row = b / KROW, phys = (b % KROW) / 16;
+      dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+      ddst[k] = (isv[k] ? TSZ : 0) + (i % NI) * 1024;
+    }
+    // the tile's offset is the SGPR offset (range-checked with the rest: rows past N read as zero)
+    auto dma = [&](int j, int stg) {
+      uint8_t* base = smem + stg * STAGE;
+      const int koff = j * BC * KROW;
+#pragma unroll
+      for (int k = 0; k < IPW; ++k) lds_dma16_asm(isv[k] ? vr : kr, base + ddst[k], dsrc[k], koff);
+    };
+    const int first = nt < 2 ? nt : 2;
+    for (int i = 0; i < first; ++i) dma(i, i);
+    // Q, dO fragments, LSE and D were loaded before the copies: they have
+    // landed once at most this wave's copies remain; the empty statement
+    // keeps the compiler's own wait for them out of the loop
+    if (first == 2) FA2_WAIT_VMCNT(2 * IPW);
+    else FA2_WAIT_VMCNT(IPW);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(qf[dk]), "v"(dof[dk]));
+    asm volatile("" ::"v"(lse2), "v"(dlt));
+    for (int j = 0; j < nt; ++j) {
+      // this wave's copies of tile j are done once only tile j+1's may remain
+      if (j + 1 < nt) FA2_WAIT_VMCNT(IPW);
+      else FA2_WAIT_VMCNT(0);
+      // every wave's tile j has landed and every wave is done with tile j-1,
+      // whose stage (j+2)%3 now receives tile j+2
+      __syncthreads();
+      if (j + 2 < nt) dma(j + 2, (j + 2) % 3);
+      tile(smem + (j % 3) * STAGE, j);
+    }
   }
 
   // ---- epilogue: dQ = scale * dQ^T (transposed back) ----------------------

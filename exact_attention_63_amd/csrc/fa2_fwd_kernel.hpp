@@ -581,20 +581,16 @@ void fa2_fwd_kernel(Args a) {
     }
     auto dma = [&](int tile, auto stage_tag) {
       constexpr int S = decltype(stage_tag)::value;
-      // The tile's offset goes into the per-lane (VGPR) offset, not the SGPR
-      // offset: the buffer range check covers the VGPR and instruction
-      // offsets only, so rows past N of a ragged last tile read as zero
-      // instead of memory past the head.
-      const uint32_t base = (uint32_t)(tile * BC * KROW);
+      const int base = tile * BC * KROW;      // uniform: the SGPR offset of the copy
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
         const int dst = (wave * NIW + k) * 1024;
         if constexpr (TL::ASMDMA) {
-          lds_dma16_asm(kr, smem + S * TSZ + dst, dsrc[k] + base, 0);
-          lds_dma16_asm(vr, smem + (NS + S) * TSZ + dst, dsrc[k] + base, 0);
+          lds_dma16_asm(kr, smem + S * TSZ + dst, dsrc[k], base);
+          lds_dma16_asm(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
         } else {
-          lds_dma16(kr, smem + S * TSZ + dst, dsrc[k] + base, 0);
-          lds_dma16(vr, smem + (NS + S) * TSZ + dst, dsrc[k] + base, 0);
+          lds_dma16(kr, smem + S * TSZ + dst, dsrc[k], base);
+          lds_dma16(vr, smem + (NS + S) * TSZ + dst, dsrc[k], base);
         }
       }
     };

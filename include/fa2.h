@@ -174,7 +174,11 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *     own the same 32 keys, one accumulating dV and the other dK (both
  *     recompute S = Q K^T);
  *   3 "dkdv_w8_split_occ2_ring4": variant 2 with its query tiles copied
- *     straight from memory into a 4-stage LDS ring, three tiles ahead.
+ *     straight from memory into a 4-stage LDS ring, three tiles ahead;
+ *   4 "dkdv_w8_split_occ2_ring4_dq_ring3", 5 "dkdv_w4_occ1_dq_ring3":
+ *     variants 3 and 1 with the dQ kernel's key tiles copied straight from
+ *     memory into a 3-stage LDS ring, two tiles ahead (variants 1-3 stage
+ *     them through registers, one tile ahead).
  * The default is variant 3 for d = 128 and variant 1 for d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
