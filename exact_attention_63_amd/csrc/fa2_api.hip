@@ -185,6 +185,7 @@ struct BwdKernels {
   bwd_fn dkdv[2][2][2];        // [bf16][d == 128][causal]
   bwd_fn dkdv_split[2][2][2];
   bwd_fn dkdv_ring[2][2][2];
+  bwd_fn dkdv_ring_sub2[2][2][2];
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
 };
@@ -198,6 +199,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_split[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, false>;
   t.dkdv_ring[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true>;
   t.dkdv_ring[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true>;
+  t.dkdv_ring_sub2[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true, 2>;
+  t.dkdv_ring_sub2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true, 2>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
@@ -218,20 +221,23 @@ const BwdKernels kBwd = make_bwd_kernels();
 // backward variants: 0 = default, 1 = one-wave-per-SIMD dK/dV kernel,
 // 2 = role-split dK/dV kernel, 3 = role-split with a 4-stage direct-copy
 // ring; 4 and 5 = variants 3 and 1 with the dQ kernel on a 3-stage
-// direct-copy ring (1-3 use the register-staged dQ kernel)
-constexpr int kNumBwdVariants = 6;
+// direct-copy ring (1-3 use the register-staged dQ kernel); 6 = variant 3
+// with 64-query tiles (two 32-query sub-blocks per barrier)
+constexpr int kNumBwdVariants = 7;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
-                                                       "dkdv_w4_occ1_dq_ring3"};
+                                                       "dkdv_w4_occ1_dq_ring3",
+                                                       "dkdv_w8_split_occ2_ring4_q64"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
-// d = 128 the role-split kernel on the direct-copy ring is fastest (headline
-// shape 2.57 against 2.95 ms per call, N = 16384 causal 10.8 against 12.1 ms);
-// at d = 64 the one-wave-per-SIMD kernel (0.13 against 0.14 ms).
+// d = 128 the role-split kernel on the direct-copy ring with 64-query tiles
+// is fastest (headline shape 2.50 against 2.71 ms per call with 32-query
+// tiles and 2.95 ms for variant 1; N = 16384 causal 10.0 against 10.9 and
+// 12.1 ms); at d = 64 variants 1 and 6 tie (0.13 ms) and 1 is kept.
 int default_bwd_variant(int d, int causal) {
   (void)causal;
-  return d == 128 ? 3 : 1;
+  return d == 128 ? 6 : 1;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -305,9 +311,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  if (vi == 2 || vi == 3 || vi == 4) {
+  if (vi == 2 || vi == 3 || vi == 4 || vi == 6) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
-    bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal] : kBwd.dkdv_ring[bf16][big][causal];
+    bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
+              : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
+                        : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {
     a.nblk = (N + KvTile::BR - 1) / KvTile::BR;

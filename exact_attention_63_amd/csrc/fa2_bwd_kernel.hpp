@@ -412,19 +412,24 @@ void fa2_bwd_dkdv_kernel(BwdArgs a) {
 // The compiler does not see the copies (with the builtin it cannot tell the
 // ring's stages apart and drains every copy in flight before each barrier).  LSE then stays in base e in LDS
 // and is scaled by log2(e) when read.
-template <bool BF16, int D, bool CAUSAL, bool RING>
+//
+// SUB: 32-query sub-blocks per tile (SUB = 2 needs RING): the sub-blocks of a
+// tile are processed one after the other with the same registers, so a tile
+// carries SUB times the MFMA work per barrier.
+template <bool BF16, int D, bool CAUSAL, bool RING, int SUB = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
   using E = Elem<BF16>;
   constexpr int T = 512, BK = 128;
-  constexpr int BQ = 32;                    // queries per tile
+  static_assert(SUB == 1 || (SUB == 2 && RING), "two sub-blocks per tile need the copy ring");
+  constexpr int BQ = 32 * SUB;              // queries per tile
   constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
   constexpr int TSZ = BQ * KROW;            // bytes of one Q (or dO) tile
   // ring stages hold 64 LSE and 64 D slots (a 4-byte copy instruction fills 64)
   constexpr int STAGE = 2 * TSZ + (RING ? 2 * 64 * 4 : 2 * BQ * 4);
   constexpr int NS = RING ? 4 : 2;
-  constexpr int CH = BQ * D / 8;            // 16-byte chunks per tile: 512 (d = 128) or 256 (d = 64)
-  static_assert(CH <= T, "one chunk per thread and tensor");
+  constexpr int CH = BQ * D / 8;            // 16-byte chunks per tile (register staging: 512 or 256)
+  static_assert(RING || CH <= T, "one chunk per thread and tensor");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -509,17 +514,19 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
   const float c = a.c;
 
   // one 32-query tile: S (and dP), then P or dS, then one product
-  auto compute = [&](const uint8_t* st, int q0, bool masked, auto role_tag) {
+  // sb: the 32-query sub-block of the tile at st (its first query is q0)
+  auto compute = [&](const uint8_t* st, int sb, int q0, bool masked, auto role_tag) {
     constexpr bool DKR = decltype(role_tag)::value;
     const uint8_t* qt = st;
     const uint8_t* dot = st + TSZ;
-    const float* l2 = (const float*)(st + 2 * TSZ);
+    const float* l2 = (const float*)(st + 2 * TSZ) + 32 * sb;
     const float* dl = l2 + (RING ? 64 : BQ);
+    const int r0 = 32 * sb;                  // first tile row of the sub-block
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      s = E::mfma(fa.fread(qt, 0, dk), kf[dk], s);
-      if constexpr (DKR) dp = E::mfma(fa.fread(dot, 0, dk), vf[dk], dp);
+      s = E::mfma(fa.fread(qt, r0, dk), kf[dk], s);
+      if constexpr (DKR) dp = E::mfma(fa.fread(dot, r0, dk), vf[dk], dp);
     }
     u32x4 pk[2];
 #pragma unroll
@@ -547,16 +554,20 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(DKR ? qt : dot, 16 * h, db), pk[h], acc[db]);
+      for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(DKR ? qt : dot, r0 + 16 * h, db), pk[h], acc[db]);
   };
 
   auto tile = [&](const uint8_t* st, int t) {
-    const int q0 = t * BQ;
-    const bool skip = CAUSAL && q0 + BQ - 1 < k_w;
-    if (!skip) {
-      const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < k_w + 31);
-      if (dk_role) compute(st, q0, masked, std::true_type{});
-      else compute(st, q0, masked, std::false_type{});
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int q0 = t * BQ + 32 * sb;
+      // every query of the sub-block precedes every key of the wave: nothing visible
+      const bool skip = CAUSAL && q0 + 31 < k_w;
+      if (!skip) {
+        const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < k_w + 31);
+        if (dk_role) compute(st, sb, q0, masked, std::true_type{});
+        else compute(st, sb, q0, masked, std::false_type{});
+      }
     }
   };
 
@@ -575,12 +586,12 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
       }
     }
   } else {
-    // Copy instructions of one tile: NI per tensor (Q, dO) of 1 KiB each, two
-    // per wave for d = 128 and one for d = 64; waves 0 and 1 also copy the 64
-    // LSE and D slots (4 bytes per lane; slots past the tile are not read).
+    // Copy instructions of one tile: NI per tensor (Q, dO) of 1 KiB each,
+    // IPW per wave; waves 0 and 1 also copy the 64 LSE and D slots (4 bytes
+    // per lane; with 32-query tiles the slots past the tile are not read).
     constexpr int NI = TSZ / 1024;
     constexpr int IPW = 2 * NI / 8;
-    static_assert(2 * NI % 8 == 0 && IPW >= 1, "tile copies must split evenly over the waves");
+    static_assert(2 * NI % 8 == 0 && IPW >= 1 && 3 * (IPW + 1) < 16, "tile copies must split evenly over the waves");
     // the wave index read from lane 0, so that the copy's buffer descriptor
     // and LDS destination (scalar operands) are known to be wave-uniform
     const int wv = __builtin_amdgcn_readfirstlane(wave);

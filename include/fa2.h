@@ -178,8 +178,10 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *   4 "dkdv_w8_split_occ2_ring4_dq_ring3", 5 "dkdv_w4_occ1_dq_ring3":
  *     variants 3 and 1 with the dQ kernel's key tiles copied straight from
  *     memory into a 3-stage LDS ring, two tiles ahead (variants 1-3 stage
- *     them through registers, one tile ahead).
- * The default is variant 3 for d = 128 and variant 1 for d = 64.
+ *     them through registers, one tile ahead);
+ *   6 "dkdv_w8_split_occ2_ring4_q64": variant 3 with 64-query tiles, each
+ *     processed as two 32-query sub-blocks between two barriers.
+ * The default is variant 6 for d = 128 and variant 1 for d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,
