@@ -110,6 +110,36 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
+BWD_SOURCES = [os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_bwd_kernel.hpp"),
+               os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_api.hip")]
+
+
+def bwd_identity(w) -> str:
+    """Hash of the backward kernel source, the host code that picks the default
+    configuration, and dtype/d/causal."""
+    h = hashlib.sha256()
+    for path in BWD_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic_bwd(w, variant: int = 0):
+    """HBM bytes per backward call from committed counter runs, or None."""
+    if variant != 0:
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("bwd:" + w.name)
+    if not ent or ent.get("kernel_identity") != bwd_identity(w):
+        return None
+    return ent.get("hbm_bytes_per_call")
+
+
 def cpu_baseline_bwd(w, budget_s: float = 20.0):
     """The fp64 CPU gradient oracle timed on whole heads of the same workload."""
     import oracle
@@ -189,7 +219,7 @@ def backward_main(args, w):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic_bwd(w, args.variant),
             "scope": "the whole call (three kernels); per-kernel durations in the rocprofv3 summary",
         },
     }

@@ -186,6 +186,7 @@ struct BwdKernels {
   bwd_fn dkdv_split[2][2][2];
   bwd_fn dkdv_ring[2][2][2];
   bwd_fn dkdv_ring_sub2[2][2][2];
+  bwd_fn dkdv_pair[2][2][2];
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
 };
@@ -201,6 +202,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_ring[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true>;
   t.dkdv_ring_sub2[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true, 2>;
   t.dkdv_ring_sub2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true, 2>;
+  t.dkdv_pair[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false>;
+  t.dkdv_pair[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
@@ -222,22 +225,25 @@ const BwdKernels kBwd = make_bwd_kernels();
 // 2 = role-split dK/dV kernel, 3 = role-split with a 4-stage direct-copy
 // ring; 4 and 5 = variants 3 and 1 with the dQ kernel on a 3-stage
 // direct-copy ring (1-3 use the register-staged dQ kernel); 6 = variant 3
-// with 64-query tiles (two 32-query sub-blocks per barrier)
-constexpr int kNumBwdVariants = 7;
+// with 64-query tiles (two 32-query sub-blocks per barrier); 7 = P handed
+// from the dV wave to the dK wave of a SIMD through LDS (no S recomputed)
+constexpr int kNumBwdVariants = 8;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
                                                        "dkdv_w4_occ1_dq_ring3",
-                                                       "dkdv_w8_split_occ2_ring4_q64"};
+                                                       "dkdv_w8_split_occ2_ring4_q64",
+                                                       "dkdv_w8_pair_occ2_ring3_q64"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
-// d = 128 the role-split kernel on the direct-copy ring with 64-query tiles
-// is fastest (headline shape 2.50 against 2.71 ms per call with 32-query
-// tiles and 2.95 ms for variant 1; N = 16384 causal 10.0 against 10.9 and
-// 12.1 ms); at d = 64 variants 1 and 6 tie (0.13 ms) and 1 is kept.
+// d = 128 the P hand-off between the two waves of a SIMD is fastest
+// (headline shape 2.40 ms per call against 2.42-2.45 for the role split
+// with 64-query tiles, 2.71 with 32-query tiles and 2.95 for variant 1;
+// N = 16384 causal 9.5 against 9.9 ms); at d = 64 variant 1 (0.129 ms against
+// 0.131-0.133 for variants 6 and 7).
 int default_bwd_variant(int d, int causal) {
   (void)causal;
-  return d == 128 ? 6 : 1;
+  return d == 128 ? 7 : 1;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -311,10 +317,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  if (vi == 2 || vi == 3 || vi == 4 || vi == 6) {
+  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
+              : vi == 7 ? kBwd.dkdv_pair[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {

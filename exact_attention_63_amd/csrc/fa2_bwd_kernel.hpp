@@ -681,6 +681,242 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV with P handed from one wave of a SIMD to the other: one workgroup per
+// (key block of 128 keys, head), 8 waves, two per SIMD; wave w owns keys
+// [k_wg + 32*(w%4), +32).  Query tiles of 64 rows (two 32-query sub-blocks),
+// copied straight from memory into a 3-stage LDS ring.  Per tile, in two
+// phases separated by a barrier:
+//   phase 1: the dV wave computes S = Q K_w^T and P = 2^(S c - LSE2) of both
+//            sub-blocks and stores the fp32 P in LDS (each lane its own 16
+//            values: the dK wave's dP registers have the same layout); the dK
+//            wave computes dP = dO V_w^T of both sub-blocks;
+//   phase 2: the dV wave accumulates dV^T += dO^T P; the dK wave reads P,
+//            forms dS = P (dP - D) and accumulates dK^T += Q^T dS.
+// Each product is computed once (8 N^2 d MFMA FLOPs per head) and both waves
+// of a SIMD issue 16 MFMAs per phase.
+template <bool BF16, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
+  using E = Elem<BF16>;
+  constexpr int BK = 128;
+  constexpr int SUB = 2;
+  constexpr int BQ = 32 * SUB;              // queries per tile
+  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
+  constexpr int TSZ = BQ * KROW;            // bytes of one Q (or dO) tile
+  constexpr int STAGE = 2 * TSZ + 2 * 64 * 4;   // Q, dO, 64 LSE slots, 64 D slots
+  constexpr int NS = 3;
+  constexpr int PSLOT = 64 * 16 * 4;        // one sub-block's fp32 P of one key group (4 KiB)
+  constexpr int PBASE = NS * STAGE;
+  constexpr int SMEM = PBASE + 4 * SUB * PSLOT;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int grp = wave & 3;                 // key group
+  // waves 4-7: dK; waves 0-3: dV (read from lane 0: the role is wave-uniform)
+  const bool dk_role = __builtin_amdgcn_readfirstlane(wave) >= 4;
+
+  int bh, kblk;
+  {
+    const int i = blockIdx.x;
+    const int total = a.nblk * a.BH;
+    if constexpr (!CAUSAL) {
+      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+      bh = logical / a.nblk;
+      kblk = logical % a.nblk;
+    } else {
+      bh = i % a.BH;
+      kblk = i / a.BH;
+    }
+  }
+  const int N = a.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  auto rsrc = [&](const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
+  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+
+  const int k_wg = kblk * BK;
+  const int k_w = k_wg + 32 * grp;
+  const int key = k_w + lr;
+
+  // the dV wave keeps the group's K rows (for S), the dK wave its V rows (for dP)
+  u32x4 bf[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk)
+    bf[dk] = __builtin_amdgcn_raw_buffer_load_b128(dk_role ? vr : kr, (uint32_t)(key * KROW + (2 * dk + lh) * 16), 0, 0);
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const int nt = (N + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? k_wg / BQ : 0;
+
+  const FragAddr<D> fa(lane);
+  const float c = a.c;
+  // this lane's P values of (key group, sub-block): 4 x 16 bytes, lane-contiguous
+  uint8_t* const pslot = smem + PBASE + grp * SUB * PSLOT + 16 * lane;
+
+  auto sub_skip = [&](int q0) { return CAUSAL && q0 + 31 < k_w; };   // sub-block entirely before the keys
+  auto sub_masked = [&](int q0) { return (q0 + 32 > N) || (CAUSAL && q0 < k_w + 31); };
+
+  // phase 1 of one tile: P to LDS (dV wave) or dP into registers (dK wave)
+  u32x4 pk[SUB][2];     // dV wave: packed P of each sub-block (B operands of dV^T += dO^T P)
+  f32x16 dp[SUB];       // dK wave: dP of each sub-block
+  auto phase1 = [&](const uint8_t* st, int t) {
+    const uint8_t* qt = st;
+    const uint8_t* dot = st + TSZ;
+    const float* l2 = (const float*)(st + 2 * TSZ);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int q0 = t * BQ + 32 * sb;
+      if (sub_skip(q0)) continue;
+      if (!dk_role) {
+        f32x16 sv = f32x16{};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) sv = E::mfma(fa.fread(qt, 32 * sb, dk), bf[dk], sv);
+        const bool masked = sub_masked(q0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lq = *(const f32x4*)(l2 + 32 * sb + 8 * g + 4 * lh) * kLog2e;
+          f32x4 pv4;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * g + b], c, -lq[b]));
+            if (masked) {
+              const int q = q0 + 8 * g + 4 * lh + b;
+              pv = (q < N && (!CAUSAL || key <= q)) ? pv : 0.f;
+            }
+            pv4[b] = pv;
+          }
+          *(f32x4*)(pslot + sb * PSLOT + g * 1024) = pv4;
+          pk[sb][g >> 1][2 * (g & 1)] = E::pack(pv4[0], pv4[1]);
+          pk[sb][g >> 1][2 * (g & 1) + 1] = E::pack(pv4[2], pv4[3]);
+        }
+      } else {
+        f32x16 d = f32x16{};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) d = E::mfma(fa.fread(dot, 32 * sb, dk), bf[dk], d);
+        dp[sb] = d;
+      }
+    }
+  };
+  // phase 2 of one tile: dV^T += dO^T P (dV wave) or dK^T += Q^T dS (dK wave)
+  auto phase2 = [&](const uint8_t* st, int t) {
+    const uint8_t* qt = st;
+    const uint8_t* dot = st + TSZ;
+    const float* dl = (const float*)(st + 2 * TSZ) + 64;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int q0 = t * BQ + 32 * sb;
+      if (sub_skip(q0)) continue;
+      if (!dk_role) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(dot, 32 * sb + 16 * h, db), pk[sb][h], acc[db]);
+      } else {
+        u32x4 ds[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 pv4 = *(const f32x4*)(pslot + sb * PSLOT + g * 1024);
+          const f32x4 dq4 = *(const f32x4*)(dl + 32 * sb + 8 * g + 4 * lh);
+          float v[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) v[b] = pv4[b] * (dp[sb][4 * g + b] - dq4[b]);
+          ds[g >> 1][2 * (g & 1)] = E::pack(v[0], v[1]);
+          ds[g >> 1][2 * (g & 1) + 1] = E::pack(v[2], v[3]);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(qt, 32 * sb + 16 * h, db), ds[h], acc[db]);
+      }
+    }
+  };
+
+  // ---- 3-stage ring of query tiles, two tiles ahead (as in the split kernel) --
+  constexpr int NI = TSZ / 1024;
+  constexpr int IPW = 2 * NI / 8;
+  static_assert(2 * NI % 8 == 0 && IPW >= 1 && 2 * (IPW + 1) < 16, "tile copies must split evenly over the waves");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dsrc[IPW];
+  int ddst[IPW];
+  bool dq_t[IPW];
+#pragma unroll
+  for (int k = 0; k < IPW; ++k) {
+    const int i = wv * IPW + k;
+    dq_t[k] = i >= NI;
+    const int b = (i % NI) * 1024 + 16 * lane;
+    const int row = b / KROW, phys = (b % KROW) / 16;
+    dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+    ddst[k] = (dq_t[k] ? TSZ : 0) + (i % NI) * 1024;
+  }
+  const bool stat_wave = wv < 2;            // wave 0: LSE, wave 1: D
+  auto dma = [&](int t, int stg) {
+    uint8_t* base = smem + stg * STAGE;
+    const int qoff = t * BQ * KROW;
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k], qoff);
+    if (stat_wave) lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * lane), t * BQ * 4);
+  };
+  if (t0 < nt) {
+    const int first = nt - t0 < 2 ? nt - t0 : 2;
+    for (int i = 0; i < first; ++i) dma(t0 + i, i);
+    // fragment loads are older than every copy (see the split kernel)
+    const int per_tile = IPW + (stat_wave ? 1 : 0);
+    if (first * per_tile >= 2 * (IPW + 1)) FA2_WAIT_VMCNT(2 * (IPW + 1));
+    else if (first * per_tile >= 2 * IPW) FA2_WAIT_VMCNT(2 * IPW);
+    else if (first * per_tile >= IPW + 1) FA2_WAIT_VMCNT(IPW + 1);
+    else if (first * per_tile >= IPW) FA2_WAIT_VMCNT(IPW);
+    else FA2_WAIT_VMCNT(0);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(bf[dk]));
+    for (int t = t0; t < nt; ++t) {
+      const int i = t - t0;
+      // this wave's copies of tile t are done once only tile t+1's may remain
+      if (t + 1 < nt) {
+        if (stat_wave) FA2_WAIT_VMCNT(IPW + 1);
+        else FA2_WAIT_VMCNT(IPW);
+      } else {
+        FA2_WAIT_VMCNT(0);
+      }
+      // every wave's copies of tile t have landed and every wave is done with
+      // tile t-1 (its stage and the P slots), whose stage now receives tile t+2
+      __syncthreads();
+      if (t + 2 < nt) dma(t + 2, (i + 2) % 3);
+      const uint8_t* st = smem + (i % 3) * STAGE;
+      phase1(st, t);
+      // the P of both sub-blocks is in LDS
+      __syncthreads();
+      phase2(st, t);
+    }
+  }
+
+  // ---- epilogue: dV = dV^T or dK = scale * dK^T, transposed back ----------
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)(dk_role ? a.dk : a.dv) + head_off), 0, head_bytes, kBufferWord3);
+  const float sc = dk_role ? a.scale : 1.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * lh;
+      u32x2 w;
+      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
+      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
+      __builtin_amdgcn_raw_buffer_store_b64(w, outr, (uint32_t)(key * KROW + d * 2), 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per (query block of 32*NW queries, head), wave w owns
 // queries [q_wg + 32w, +32).  Key tiles of 64 rows: K and V (row-major,
 // swizzled) staged in LDS.  RING = false: two stages, register-staged copies

@@ -180,8 +180,11 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *     memory into a 3-stage LDS ring, two tiles ahead (variants 1-3 stage
  *     them through registers, one tile ahead);
  *   6 "dkdv_w8_split_occ2_ring4_q64": variant 3 with 64-query tiles, each
- *     processed as two 32-query sub-blocks between two barriers.
- * The default is variant 6 for d = 128 and variant 1 for d = 64.
+ *     processed as two 32-query sub-blocks between two barriers;
+ *   7 "dkdv_w8_pair_occ2_ring3_q64": the dV wave of a SIMD computes S and P
+ *     and hands the fp32 P to the dK wave through LDS, so no product is
+ *     computed twice; 64-query tiles on a 3-stage copy ring.
+ * The default is variant 7 for d = 128 and variant 1 for d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -118,7 +118,7 @@ def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 31, 64, 65, 127, 129, 200, 513])
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7])
 def test_backward_edge_shapes(variant, N, d, causal, dtype):
     """Ragged N (partial query and key tiles, partial workgroups), single rows,
     for every dK/dV configuration."""
@@ -129,14 +129,14 @@ def test_backward_edge_shapes(variant, N, d, causal, dtype):
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7])
 def test_backward_scales(variant, scale, causal):
     """Zero and negative scales (P uniform over the visible keys; sign flips)."""
     run_case(f"v{variant} scale={scale} causal={causal}", 1, 2, 300, 128, "bf16", causal, scale, seed=31,
              variant=variant)
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7])
 def test_backward_batch_heads_layout(variant):
     """Several batches and heads in one launch: each head's gradients land in its own slab."""
     run_case(f"v{variant} B=3 H=5", 3, 5, 192, 64, "fp16", True, 0.125, seed=41, variant=variant)
@@ -209,6 +209,30 @@ def test_backward_column_sums():
     print(f"max|sum dK|={np.abs(sk).max():.3e}, max|sum dV - sum dO|={np.abs(sv).max():.3e}", flush=True)
     assert np.all(np.abs(sk) <= tol_k)
     assert np.all(np.abs(sv) <= tol_v)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_typed_entry_points_match(dtype):
+    """fa2_bwd_fp16 / fa2_bwd_bf16 and fa2_bwd (with dtype) give the same bits as the binding."""
+    B, H, N, d = 1, 3, 300, 128
+    q, k, v = (x.cuda() for x in make_inputs(B, H, N, d, dtype, seed=71))
+    do = make_grad_output(B, H, N, d, dtype, seed=71).cuda()
+    o, lse = fa2.forward(q, k, v, causal=True)
+    ref = fa2.backward(q, k, v, o, lse, do, causal=True)
+    lib = fa2.lib()
+    code = fa2.FA2_DTYPE_FP16 if dtype == "fp16" else fa2.FA2_DTYPE_BF16
+    typed = lib.fa2_bwd_fp16 if dtype == "fp16" else lib.fa2_bwd_bf16
+    stream = torch.cuda.current_stream().cuda_stream
+    scale = 1.0 / math.sqrt(d)
+    for call in ("typed", "generic"):
+        outs = [torch.empty_like(q) for _ in range(3)] + [torch.empty_like(lse)]
+        args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                *(t.data_ptr() for t in outs), B, H, N, d, 1, scale, stream]
+        rc = typed(*args) if call == "typed" else lib.fa2_bwd(*args, code)
+        assert rc == fa2.FA2_OK
+        torch.cuda.synchronize()
+        for x, y in zip(outs, ref):
+            assert torch.equal(x, y), call
 
 
 def test_backward_empty_problem():
