@@ -922,7 +922,10 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
 // swizzled) staged in LDS.  RING = false: two stages, register-staged copies
 // one tile ahead; RING = true: three stages filled straight from memory by
 // inline-assembly copies two tiles ahead (as in the dK/dV ring).
-template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false>
+//
+// LOOK > 0: the MFMAs of each phase are issued in a fixed order with LOOK
+// operand reads ahead (scheduling-group barriers), as in the forward pass.
+template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false, int LOOK = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(TL::THREADS, TL::THREADS),
                           amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void fa2_bwd_dq_kernel(BwdArgs a) {
@@ -1038,6 +1041,16 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
         dp[kb] = E::mfma(fa.fread(vt, 32 * kb, dk), dof[dk], dp[kb]);
       }
     }
+    if constexpr (LOOK > 0) {
+      // one 16-byte operand read per MFMA, LOOK reads ahead
+      constexpr int NM = 2 * NKB * DK;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < NM - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    }
     // P^T = 2^(s*c - LSE2), dS^T = P^T * (dP^T - D), packed (registers
     // [8h, 8h+8) = 16-key step h)
     u32x4 dsp[NKB][2];
@@ -1066,6 +1079,17 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(kt, 32 * kb + 16 * h, db), dsp[kb][h], acc[db]);
+    if constexpr (LOOK > 0) {
+      // two transpose reads per MFMA, 2*LOOK reads ahead
+      constexpr int NM = DB * NKB * 2;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < NM - LOOK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LOOK, 0);
+    }
   };
 
   auto tile = [&](const uint8_t* st, int j) {
