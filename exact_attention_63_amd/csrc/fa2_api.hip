@@ -187,6 +187,7 @@ struct BwdKernels {
   bwd_fn dkdv_ring[2][2][2];
   bwd_fn dkdv_ring_sub2[2][2][2];
   bwd_fn dkdv_pair[2][2][2];
+  bwd_fn dkdv_pair_look[2][2][2];
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
   bwd_fn dq_look[2][2][2];
@@ -205,6 +206,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_ring_sub2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true, 2>;
   t.dkdv_pair[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false>;
   t.dkdv_pair[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true>;
+  t.dkdv_pair_look[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 4>;
+  t.dkdv_pair_look[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 4>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
@@ -230,26 +233,28 @@ const BwdKernels kBwd = make_bwd_kernels();
 // direct-copy ring (1-3 use the register-staged dQ kernel); 6 = variant 3
 // with 64-query tiles (two 32-query sub-blocks per barrier); 7 = P handed
 // from the dV wave to the dK wave of a SIMD through LDS (no S recomputed);
-// 8 = variant 7 with the dQ kernel's MFMAs issued with 4 operand reads ahead
-constexpr int kNumBwdVariants = 9;
+// 8 = variant 7 with the dQ kernel's MFMAs issued with 4 operand reads ahead;
+// 9 = variant 8 with the dK/dV kernel's MFMAs ordered the same way
+constexpr int kNumBwdVariants = 10;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
                                                        "dkdv_w4_occ1_dq_ring3",
                                                        "dkdv_w8_split_occ2_ring4_q64",
                                                        "dkdv_w8_pair_occ2_ring3_q64",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_dq_look4"};
+                                                       "dkdv_w8_pair_occ2_ring3_q64_dq_look4",
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
-// d = 128 the P hand-off between the two waves of a SIMD with the dQ MFMAs
-// issued 4 operand reads ahead is fastest (headline shape 2.37-2.38 ms per
-// call against 2.41-2.42 without the dQ order, 2.42-2.45 for the role split
-// with 64-query tiles, 2.71 with 32-query tiles and 2.95 for variant 1;
-// N = 16384 causal 9.4-9.5 against 9.5 and 9.9 ms); at d = 64 variant 1
-// (0.129 ms against 0.131-0.133 for variants 6 and 7).
+// d = 128 the P hand-off between the two waves of a SIMD with every MFMA
+// phase issued 4 operand reads ahead is fastest (headline shape 2.345 ms per
+// call against 2.375-2.385 with the order in the dQ kernel only, 2.41-2.42
+// with neither, 2.42-2.45 for the role split with 64-query tiles, 2.71 with
+// 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.129 ms
+// against 0.131-0.133 for variants 6 and 7).
 int default_bwd_variant(int d, int causal) {
   (void)causal;
-  return d == 128 ? 8 : 1;
+  return d == 128 ? 9 : 1;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -323,11 +328,12 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8) {
+  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
               : (vi == 7 || vi == 8) ? kBwd.dkdv_pair[bf16][big][causal]
+              : vi == 9 ? kBwd.dkdv_pair_look[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {
@@ -339,7 +345,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
 
   a.nblk = (N + QTile::BR - 1) / QTile::BR;
   bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
-               : vi == 8               ? kBwd.dq_look[bf16][big][causal]
+               : (vi == 8 || vi == 9)  ? kBwd.dq_look[bf16][big][causal]
                                        : kBwd.dq[bf16][big][causal];
   hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;

@@ -694,7 +694,10 @@ void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
 //            forms dS = P (dP - D) and accumulates dK^T += Q^T dS.
 // Each product is computed once (8 N^2 d MFMA FLOPs per head) and both waves
 // of a SIMD issue 16 MFMAs per phase.
-template <bool BF16, int D, bool CAUSAL>
+//
+// LOOK > 0: the MFMAs of each phase are issued in a fixed order with LOOK
+// operand reads ahead (scheduling-group barriers).
+template <bool BF16, int D, bool CAUSAL, int LOOK = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
   using E = Elem<BF16>;
@@ -765,6 +768,31 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
 
   auto sub_skip = [&](int q0) { return CAUSAL && q0 + 31 < k_w; };   // sub-block entirely before the keys
   auto sub_masked = [&](int q0) { return (q0 + 32 > N) || (CAUSAL && q0 < k_w + 31); };
+  // issue order of DK MFMAs fed by one 16-byte read each, LOOK reads ahead
+  auto order_fread = [&]() {
+    if constexpr (LOOK > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < DK - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    }
+  };
+  // issue order of 2*DB MFMAs fed by two transpose reads each, LOOK MFMAs ahead
+  auto order_tread = [&]() {
+    if constexpr (LOOK > 0) {
+      constexpr int NM = 2 * DB;
+      constexpr int LA = LOOK < NM ? LOOK : NM;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LA, 0);
+#pragma unroll
+      for (int i = 0; i < NM - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LA, 0);
+    }
+  };
 
   // phase 1 of one tile: P to LDS (dV wave) or dP into registers (dK wave)
   u32x4 pk[SUB][2];     // dV wave: packed P of each sub-block (B operands of dV^T += dO^T P)
@@ -781,6 +809,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
         f32x16 sv = f32x16{};
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) sv = E::mfma(fa.fread(qt, 32 * sb, dk), bf[dk], sv);
+        order_fread();
         const bool masked = sub_masked(q0);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -803,6 +832,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
         f32x16 d = f32x16{};
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) d = E::mfma(fa.fread(dot, 32 * sb, dk), bf[dk], d);
+        order_fread();
         dp[sb] = d;
       }
     }
@@ -821,6 +851,7 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(dot, 32 * sb + 16 * h, db), pk[sb][h], acc[db]);
+        order_tread();
       } else {
         u32x4 ds[2];
 #pragma unroll

@@ -185,8 +185,10 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *     and hands the fp32 P to the dK wave through LDS, so no product is
  *     computed twice; 64-query tiles on a 3-stage copy ring;
  *   8 "dkdv_w8_pair_occ2_ring3_q64_dq_look4": variant 7 with the dQ
- *     kernel's MFMAs issued in a fixed order, 4 operand reads ahead.
- * The default is variant 8 for d = 128 and variant 1 for d = 64.
+ *     kernel's MFMAs issued in a fixed order, 4 operand reads ahead;
+ *   9 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4": variant 8 with the
+ *     dK/dV kernel's MFMAs ordered the same way.
+ * The default is variant 9 for d = 128 and variant 1 for d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,
