@@ -191,6 +191,7 @@ struct BwdKernels {
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
   bwd_fn dq_look[2][2][2];
+  bwd_fn dq_look_fused[2][2][2];
 };
 
 template <bool BF16, int D>
@@ -214,6 +215,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dq_ring[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, true>;
   t.dq_look[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4>;
   t.dq_look[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4>;
+  t.dq_look_fused[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4, true>;
+  t.dq_look_fused[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4, true>;
 }
 
 BwdKernels make_bwd_kernels() {
@@ -234,8 +237,10 @@ const BwdKernels kBwd = make_bwd_kernels();
 // with 64-query tiles (two 32-query sub-blocks per barrier); 7 = P handed
 // from the dV wave to the dK wave of a SIMD through LDS (no S recomputed);
 // 8 = variant 7 with the dQ kernel's MFMAs issued with 4 operand reads ahead;
-// 9 = variant 8 with the dK/dV kernel's MFMAs ordered the same way
-constexpr int kNumBwdVariants = 10;
+// 9 = variant 8 with the dK/dV kernel's MFMAs ordered the same way;
+// 10 = variant 9 with D computed by the dQ kernel, which runs first (two
+// launches instead of three)
+constexpr int kNumBwdVariants = 11;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
@@ -243,7 +248,8 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w8_split_occ2_ring4_q64",
                                                        "dkdv_w8_pair_occ2_ring3_q64",
                                                        "dkdv_w8_pair_occ2_ring3_q64_dq_look4",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4"};
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4",
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD with every MFMA
@@ -320,20 +326,36 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
 
-  // D = rowsum(dO * O): one lane per 8 elements
-  const long long rows = (long long)(bh * (uint64_t)N);
-  const uint64_t lanes = (uint64_t)rows * (uint64_t)(d / 8);
-  a.nblk = 0;
-  hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
-  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
-
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9) {
+  const bool fused_d = vi == 10;
+  auto launch_dq = [&]() {
+    a.nblk = (N + QTile::BR - 1) / QTile::BR;
+    bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
+                 : (vi == 8 || vi == 9) ? kBwd.dq_look[bf16][big][causal]
+                 : vi == 10             ? kBwd.dq_look_fused[bf16][big][causal]
+                                        : kBwd.dq[bf16][big][causal];
+    hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
+    return hipGetLastError() == hipSuccess;
+  };
+
+  if (fused_d) {
+    // dQ first: it computes D, uses it and writes it for the dK/dV kernel
+    if (!launch_dq()) return FA2_ERR_LAUNCH;
+  } else {
+    // D = rowsum(dO * O): one lane per 8 elements
+    const long long rows = (long long)(bh * (uint64_t)N);
+    const uint64_t lanes = (uint64_t)rows * (uint64_t)(d / 8);
+    a.nblk = 0;
+    hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
+    if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+  }
+
+  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
               : (vi == 7 || vi == 8) ? kBwd.dkdv_pair[bf16][big][causal]
-              : vi == 9 ? kBwd.dkdv_pair_look[bf16][big][causal]
+              : (vi == 9 || vi == 10) ? kBwd.dkdv_pair_look[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {
@@ -343,12 +365,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   }
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
-  a.nblk = (N + QTile::BR - 1) / QTile::BR;
-  bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
-               : (vi == 8 || vi == 9)  ? kBwd.dq_look[bf16][big][causal]
-                                       : kBwd.dq[bf16][big][causal];
-  hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+  if (!fused_d && !launch_dq()) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }
 

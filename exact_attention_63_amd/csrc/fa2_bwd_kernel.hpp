@@ -956,7 +956,12 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
 //
 // LOOK > 0: the MFMAs of each phase are issued in a fixed order with LOOK
 // operand reads ahead (scheduling-group barriers), as in the forward pass.
-template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false, int LOOK = 0>
+// FUSED_D: the kernel computes D_i = dO_i . O_i itself from the dO row it
+// holds and the O row it loads (each lane half holds half of the row; one
+// exchange between lane l and l^32 completes the sum), uses it, and writes
+// it to delta for the dK/dV kernel, which then runs after this one; the
+// separate D kernel is not launched.
+template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false, int LOOK = 0, bool FUSED_D = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(TL::THREADS, TL::THREADS),
                           amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void fa2_bwd_dq_kernel(BwdArgs a) {
@@ -1016,7 +1021,24 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
       (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
   const float lse2 =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lser, (uint32_t)(q * 4), 0, 0)) * kLog2e;
-  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
+  float dlt;
+  if constexpr (FUSED_D) {
+    const __amdgpu_buffer_rsrc_t orr = rsrc(a.o);
+    float part = 0.f;
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const u32x4 ov = __builtin_amdgcn_raw_buffer_load_b128(orr, (uint32_t)(q * KROW + (2 * dk + lh) * 16), 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        part = __builtin_fmaf(half_lo<BF16>(ov[t]), half_lo<BF16>(dof[dk][t]), part);
+        part = __builtin_fmaf(half_hi<BF16>(ov[t]), half_hi<BF16>(dof[dk][t]), part);
+      }
+    }
+    dlt = sum_halves(part);
+    if (lh == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dlt), dlr, (uint32_t)(q * 4), 0, 0);
+  } else {
+    dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
+  }
 
   f32x16 acc[DB];
 #pragma unroll

@@ -187,7 +187,10 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *   8 "dkdv_w8_pair_occ2_ring3_q64_dq_look4": variant 7 with the dQ
  *     kernel's MFMAs issued in a fixed order, 4 operand reads ahead;
  *   9 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4": variant 8 with the
- *     dK/dV kernel's MFMAs ordered the same way.
+ *     dK/dV kernel's MFMAs ordered the same way;
+ *   10 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d": variant 9 with
+ *     D computed inside the dQ kernel, which then runs first (two kernels
+ *     instead of three; delta is written all the same).
  * The default is variant 9 for d = 128 and variant 1 for d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
