@@ -110,17 +110,20 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
-BWD_SOURCES = [os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_bwd_kernel.hpp"),
-               os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_api.hip")]
+BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_bwd_kernel.hpp")
+API_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_api.hip")
 
 
 def bwd_identity(w) -> str:
-    """Hash of the backward kernel source, the host code that picks the default
-    configuration, and dtype/d/causal."""
+    """Hash of the backward kernel source, the host function that picks the
+    default backward configuration, and dtype/d/causal."""
+    import re
     h = hashlib.sha256()
-    for path in BWD_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    with open(BWD_KERNEL_SOURCE, "rb") as f:
+        h.update(f.read())
+    with open(API_SOURCE) as f:
+        m = re.search(r"int default_bwd_variant\(.*?\n}", f.read(), flags=re.S)
+    h.update((m.group(0) if m else "").encode())
     h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
     return h.hexdigest()[:16]
 

@@ -12,6 +12,7 @@
 #include "fa2.h"
 #include "fa2_fwd_kernel.hpp"
 #include "fa2_bwd_kernel.hpp"
+#include "fa2_fwd_roles.hpp"
 
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -41,6 +42,17 @@ constexpr Variant make_variant(const char* name) {
                    {fa2::fa2_fwd_kernel<true, 128, false, TL>, fa2::fa2_fwd_kernel<true, 128, true, TL>}}}};
 }
 
+// The role-split kernel (fa2_fwd_roles.hpp): 8 waves, 128 queries per workgroup.
+constexpr Variant make_roles_variant(const char* name) {
+  return Variant{name,
+                 512,
+                 128,
+                 {{{fa2::fa2_fwd_roles_kernel<false, 64, false>, fa2::fa2_fwd_roles_kernel<false, 64, true>},
+                   {fa2::fa2_fwd_roles_kernel<false, 128, false>, fa2::fa2_fwd_roles_kernel<false, 128, true>}},
+                  {{fa2::fa2_fwd_roles_kernel<true, 64, false>, fa2::fa2_fwd_roles_kernel<true, 64, true>},
+                   {fa2::fa2_fwd_roles_kernel<true, 128, false>, fa2::fa2_fwd_roles_kernel<true, 128, true>}}}};
+}
+
 // Index 0 is the tuned default; it is resolved per (dtype, d, causal) by
 // default_variant() below.
 const Variant kVariants[] = {
@@ -68,6 +80,7 @@ const Variant kVariants[] = {
     make_variant<Tile<4, 1, 2, 2, 5, 4>>("w4_q32_k64_dma2_look4"),   // 4 waves, 2 workgroups per CU, 4 operand reads ahead
     make_variant<Tile<8, 1, 2, 2, 10, 0, 4>>("w8_q32_k32_dma4_thread4"),   // softmax threaded between MFMAs, 4 operands ahead
     make_variant<Tile<8, 1, 2, 2, 11, 4>>("w8_q32_k64_dma3_shift_look4"),  // waves 0-3 one phase ahead of waves 4-7
+    make_roles_variant("w8_pairs32_k64_roles_ring3"),  // softmax wave + P.V wave per SIMD, P through LDS
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
