@@ -115,12 +115,13 @@ API_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_api.hip")
 
 
 def bwd_identity(w) -> str:
-    """Hash of the backward kernel source, the host function that picks the
-    default backward configuration, and dtype/d/causal."""
+    """Hash of the backward kernel source (without its // comments, whitespace
+    collapsed), the host function that picks the default backward
+    configuration, and dtype/d/causal."""
     import re
     h = hashlib.sha256()
-    with open(BWD_KERNEL_SOURCE, "rb") as f:
-        h.update(f.read())
+    with open(BWD_KERNEL_SOURCE) as f:
+        h.update(" ".join(re.sub(r"//[^\n]*", "", f.read()).split()).encode())
     with open(API_SOURCE) as f:
         m = re.search(r"int default_bwd_variant\(.*?\n}", f.read(), flags=re.S)
     h.update((m.group(0) if m else "").encode())

@@ -15,11 +15,15 @@
 // Three kernels, all enqueued on the caller's stream:
 //   * fa2_bwd_delta_kernel: D_i = dO_i . O_i (fp32), one row per 8 or 16
 //     lanes, written to the caller's delta buffer;
-//   * fa2_bwd_dkdv_kernel: one workgroup per (key block, head); each wave
-//     owns 32 keys (the sliced-Q split of the forward pass, with keys in the
-//     place of queries), keeps their K and V rows in VGPRs and their dK^T,
-//     dV^T accumulators in registers, and walks the query tiles (Q, dO, LSE
-//     and D staged in LDS, double-buffered);
+//   * dK/dV: one workgroup per (key block, head); 32 keys per wave or per
+//     pair of waves (the sliced-Q split of the forward pass, with keys in the
+//     place of queries); K, V rows in VGPRs, dK^T, dV^T accumulators in
+//     registers; the query tiles (Q, dO, LSE and D) walk through LDS.  Three
+//     configurations: fa2_bwd_dkdv_kernel (each wave accumulates both, one
+//     wave per SIMD), fa2_bwd_dkdv_split_kernel (the two waves of a SIMD
+//     accumulate dV and dK of the same keys, both computing S) and
+//     fa2_bwd_dkdv_pair_kernel (the dV wave hands P to the dK wave through
+//     LDS, so every product is computed once);
 //   * fa2_bwd_dq_kernel: one workgroup per (query block, head); each wave
 //     owns 32 queries, keeps their Q and dO rows in VGPRs and the dQ^T
 //     accumulator in registers, and walks the key tiles (K, V in LDS).
