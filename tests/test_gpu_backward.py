@@ -6,21 +6,10 @@ plus the seeded dO.  Its outputs are compared with ``oracle.attention_backward``
 (fp64, from Q, K, V and dO alone).
 
 Tolerance.  The pages give none for gradients, so each element gets a bound
-derived from the arithmetic the kernels perform, with u the unit roundoff of
-the input dtype (bf16 2^-8, fp16 2^-11):
-  * P is recomputed in fp32 (relative error ~1e-6, far below u) and rounded
-    to the dtype for dV = P^T dO:      |dV err| <= u (P^T |dO|) + u |dV|;
-  * D = rowsum(dO * O) uses the rounded O: |D err|_i <= u a_i with
-    a_i = sum_t |dO_it| |O_it|;
-  * dS = P (dP - D) is rounded to the dtype for the two products:
-    |dS err|_ij <= u (|dS_ij| + P_ij a_i) =: E_ij;
-  * |dK err| <= |scale| (E^T |Q|) + u |dK|,  |dQ err| <= |scale| (E |K|) + u |dQ|
-    (the last term is the final rounding to the dtype).
-Each element must satisfy |gpu - oracle| <= 2 * bound + 1e-5 * max|oracle|
-(the factor 2 covers second-order terms and fp32 accumulation, whose error is
-~d * 2^-24 relative).  D itself is fp32: |D err| <= u a_i + 1e-5 a_i.
-A wrong index, sign or operand produces errors of the size of the terms
-themselves, orders of magnitude above these bounds.
+derived from the arithmetic the kernels perform (tests/bwd_bounds.py: the
+rounding of P, dS, O and the outputs to the input dtype).  The CPU test
+tests/test_backward_bound.py pins the bound itself: a model of the kernels'
+rounding stays inside it, and planted mistakes break it.
 """
 
 import math
@@ -31,11 +20,10 @@ import torch
 
 import exact_attention_63_amd as fa2
 import oracle
+from bwd_bounds import UNIT, head_bounds, worst_ratio
 from workloads import WORKLOADS, make_grad_output, make_inputs, to_f64, workload_grad_output, workload_inputs
 
 pytestmark = pytest.mark.gpu
-
-UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -51,30 +39,9 @@ def oracle_forward_inputs(q64, k64, v64, causal, scale, dtype):
     return torch.from_numpy(o).to(td), torch.from_numpy(lse).to(torch.float32)
 
 
-def head_bounds(q, k, v, o_r, do, causal, scale, dtype, ref):
-    """Elementwise error bounds for one head (fp64 arrays [N, d]); ref = oracle (dq, dk, dv, delta)."""
-    u = UNIT[dtype]
-    n = q.shape[0]
-    vis = oracle.visible_mask(np.arange(n), n, causal)
-    s = np.where(vis, scale * (q @ k.T), -np.inf)
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    p = e / e.sum(axis=1, keepdims=True)
-    dq, dk, dv, delta = ref
-    ds = p * ((do @ v.T) - delta[:, None])
-    a = (np.abs(do) * np.abs(o_r)).sum(axis=1)
-    E = u * (np.abs(ds) + p * a[:, None])
-    b_dv = u * (p.T @ np.abs(do)) + u * np.abs(dv)
-    b_dk = abs(scale) * (E.T @ np.abs(q)) + u * np.abs(dk)
-    b_dq = abs(scale) * (E @ np.abs(k)) + u * np.abs(dq)
-    b_delta = (u + 1e-5) * a
-    return b_dq, b_dk, b_dv, b_delta
-
-
 def compare(name, got, ref, bound):
     err = np.abs(got - ref)
-    tol = 2.0 * bound + 1e-5 * max(np.abs(ref).max(), 1e-30)
-    ratio = (err / tol).max() if err.size else 0.0
+    ratio = worst_ratio(got, ref, bound)
     print(f"  {name}: max|err|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
           f"worst err/tol={ratio:.3f}", flush=True)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
