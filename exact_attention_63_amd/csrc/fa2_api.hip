@@ -188,6 +188,8 @@ typedef void (*delta_fn)(BwdArgs, long long);
 // dQ kernel: 8 waves (256 queries) per workgroup, two waves per SIMD.
 using KvTile = BwdTile<4, 1>;
 using QTile = BwdTile<8, 2>;
+// dQ alternative for small grids: 4 waves (128 queries) per workgroup
+using QTile4 = BwdTile<4, 2>;
 
 // dK/dV alternative: 8 waves (128 keys), two per SIMD, the dV and dK
 // products split between the two waves of a SIMD.
@@ -205,6 +207,7 @@ struct BwdKernels {
   bwd_fn dq_ring[2][2][2];
   bwd_fn dq_look[2][2][2];
   bwd_fn dq_look_fused[2][2][2];
+  bwd_fn dq4_look[2][2];       // [bf16][causal], d = 64 only
 };
 
 template <bool BF16, int D>
@@ -234,6 +237,10 @@ constexpr void fill_bwd(BwdKernels& t) {
 
 BwdKernels make_bwd_kernels() {
   BwdKernels t{};
+  t.dq4_look[0][0] = fa2::fa2_bwd_dq_kernel<false, 64, false, QTile4, false, 4>;
+  t.dq4_look[0][1] = fa2::fa2_bwd_dq_kernel<false, 64, true, QTile4, false, 4>;
+  t.dq4_look[1][0] = fa2::fa2_bwd_dq_kernel<true, 64, false, QTile4, false, 4>;
+  t.dq4_look[1][1] = fa2::fa2_bwd_dq_kernel<true, 64, true, QTile4, false, 4>;
   fill_bwd<false, 64>(t);
   fill_bwd<false, 128>(t);
   fill_bwd<true, 64>(t);
@@ -252,8 +259,10 @@ const BwdKernels kBwd = make_bwd_kernels();
 // 8 = variant 7 with the dQ kernel's MFMAs issued with 4 operand reads ahead;
 // 9 = variant 8 with the dK/dV kernel's MFMAs ordered the same way;
 // 10 = variant 9 with D computed by the dQ kernel, which runs first (two
-// launches instead of three)
-constexpr int kNumBwdVariants = 11;
+// launches instead of three); 11 = variant 1 with 4-wave (128-query) dQ
+// workgroups, MFMAs 4 operand reads ahead (at d = 128 it runs variant 1's
+// dQ kernel)
+constexpr int kNumBwdVariants = 12;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
@@ -262,18 +271,21 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w8_pair_occ2_ring3_q64",
                                                        "dkdv_w8_pair_occ2_ring3_q64_dq_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d"};
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d",
+                                                       "dkdv_w4_occ1_dq_w4_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD with every MFMA
 // phase issued 4 operand reads ahead is fastest (headline shape 2.345 ms per
 // call against 2.375-2.385 with the order in the dQ kernel only, 2.41-2.42
 // with neither, 2.42-2.45 for the role split with 64-query tiles, 2.71 with
-// 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.129 ms
-// against 0.131-0.133 for variants 6 and 7).
+// 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
+// against 0.130-0.133 for variants 6, 7 and 11), and for causal d = 64
+// variant 11, whose 4-wave dQ workgroups balance the triangular work
+// (0.095 against 0.103 ms).
 int default_bwd_variant(int d, int causal) {
-  (void)causal;
-  return d == 128 ? 9 : 1;
+  if (d == 128) return 9;
+  return causal ? 11 : 1;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -342,6 +354,12 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
   const bool fused_d = vi == 10;
   auto launch_dq = [&]() {
+    if (vi == 11 && !big) {
+      a.nblk = (N + QTile4::BR - 1) / QTile4::BR;
+      hipLaunchKernelGGL(kBwd.dq4_look[bf16][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
+                         dim3(QTile4::THREADS), 0, stream, a);
+      return hipGetLastError() == hipSuccess;
+    }
     a.nblk = (N + QTile::BR - 1) / QTile::BR;
     bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
                  : (vi == 8 || vi == 9) ? kBwd.dq_look[bf16][big][causal]

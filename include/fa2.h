@@ -190,8 +190,12 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *     dK/dV kernel's MFMAs ordered the same way;
  *   10 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d": variant 9 with
  *     D computed inside the dQ kernel, which then runs first (two kernels
- *     instead of three; delta is written all the same).
- * The default is variant 9 for d = 128 and variant 1 for d = 64.
+ *     instead of three; delta is written all the same);
+ *   11 "dkdv_w4_occ1_dq_w4_look4": variant 1 with 4-wave (128-query) dQ
+ *     workgroups at d = 64 (twice the workgroups for small grids); at
+ *     d = 128 it is variant 1.
+ * The default is variant 9 for d = 128, variant 1 for non-causal d = 64 and
+ * variant 11 for causal d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,
