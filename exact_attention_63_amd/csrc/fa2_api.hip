@@ -203,9 +203,13 @@ struct BwdKernels {
   bwd_fn dkdv_ring_sub2[2][2][2];
   bwd_fn dkdv_pair[2][2][2];
   bwd_fn dkdv_pair_look[2][2][2];
+  bwd_fn dkdv_pair_look2[2][2][2];
+  bwd_fn dkdv_pair_look6[2][2][2];
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
   bwd_fn dq_look[2][2][2];
+  bwd_fn dq_look2[2][2][2];
+  bwd_fn dq_look6[2][2][2];
   bwd_fn dq_look_fused[2][2][2];
   bwd_fn dq4_look[2][2];       // [bf16][causal], d = 64 only
 };
@@ -225,12 +229,20 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_pair[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true>;
   t.dkdv_pair_look[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 4>;
   t.dkdv_pair_look[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 4>;
+  t.dkdv_pair_look2[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 2>;
+  t.dkdv_pair_look2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 2>;
+  t.dkdv_pair_look6[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 6>;
+  t.dkdv_pair_look6[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 6>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
   t.dq_ring[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, true>;
   t.dq_look[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4>;
   t.dq_look[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4>;
+  t.dq_look2[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 2>;
+  t.dq_look2[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 2>;
+  t.dq_look6[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 6>;
+  t.dq_look6[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 6>;
   t.dq_look_fused[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4, true>;
   t.dq_look_fused[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4, true>;
 }
@@ -261,8 +273,8 @@ const BwdKernels kBwd = make_bwd_kernels();
 // 10 = variant 9 with D computed by the dQ kernel, which runs first (two
 // launches instead of three); 11 = variant 1 with 4-wave (128-query) dQ
 // workgroups, MFMAs 4 operand reads ahead (at d = 128 it runs variant 1's
-// dQ kernel)
-constexpr int kNumBwdVariants = 12;
+// dQ kernel); 12, 13 = variant 9 with 2 and 6 operand reads ahead
+constexpr int kNumBwdVariants = 14;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
@@ -272,7 +284,9 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w8_pair_occ2_ring3_q64_dq_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d",
-                                                       "dkdv_w4_occ1_dq_w4_look4"};
+                                                       "dkdv_w4_occ1_dq_w4_look4",
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look2_dq_look2",
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD with every MFMA
@@ -364,6 +378,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
                  : (vi == 8 || vi == 9) ? kBwd.dq_look[bf16][big][causal]
                  : vi == 10             ? kBwd.dq_look_fused[bf16][big][causal]
+                 : vi == 12             ? kBwd.dq_look2[bf16][big][causal]
+                 : vi == 13             ? kBwd.dq_look6[bf16][big][causal]
                                         : kBwd.dq[bf16][big][causal];
     hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
     return hipGetLastError() == hipSuccess;
@@ -381,12 +397,15 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   }
 
-  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10) {
+  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10 || vi == 12 ||
+      vi == 13) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
               : (vi == 7 || vi == 8) ? kBwd.dkdv_pair[bf16][big][causal]
               : (vi == 9 || vi == 10) ? kBwd.dkdv_pair_look[bf16][big][causal]
+              : vi == 12 ? kBwd.dkdv_pair_look2[bf16][big][causal]
+              : vi == 13 ? kBwd.dkdv_pair_look6[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {
