@@ -81,6 +81,8 @@ const Variant kVariants[] = {
     make_variant<Tile<8, 1, 2, 2, 10, 0, 4>>("w8_q32_k32_dma4_thread4"),   // softmax threaded between MFMAs, 4 operands ahead
     make_variant<Tile<8, 1, 2, 2, 11, 4>>("w8_q32_k64_dma3_shift_look4"),  // waves 0-3 one phase ahead of waves 4-7
     make_roles_variant("w8_pairs32_k64_roles_ring3"),  // softmax wave + P.V wave per SIMD, P through LDS
+    make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 1>>("w8_q32_k64_dma3_look4_swexp"),      // variant 11, every 2^x in software
+    make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 2>>("w8_q32_k64_dma3_look4_swexp_half"), // variant 11, every other 2^x in software
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

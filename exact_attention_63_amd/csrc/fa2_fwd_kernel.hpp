@@ -159,6 +159,25 @@ __device__ __forceinline__ void lds_dma16_asm(__amdgpu_buffer_rsrc_t r, uint8_t*
                : "memory", "m0");
 }
 
+// 2^x on the FMA pipe instead of the transcendental unit: the software exp2
+// of the "FlashAttention v4 Blackwell pipeline co-design" diagram, kept here
+// as a measured alternative (Tile::SWEXP).  x = n + f with n = floor(x) and
+// f in [0, 1); 2^f from a degree-4 polynomial fitted to the relative error on
+// [0, 1] (gen_exp2_poly.py: at most 2.9e-6, far below the 2^-9 rounding of P
+// to bf16); 2^n applied with ldexp.  Arguments below -126 (masked scores are
+// -inf) give exactly 0.  The softmax arguments never exceed 8.
+__device__ __forceinline__ float sw_exp2(float x) {
+  const float xc = fmaxf(x, -127.f);
+  const float n = __builtin_floorf(xc);
+  const float f = xc - n;
+  float p = __builtin_fmaf(0.013426551595330238f, f, 0.052240896970033646f);
+  p = __builtin_fmaf(p, f, 0.24128268659114838f);
+  p = __builtin_fmaf(p, f, 0.6930440068244934f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  const float r = __builtin_ldexpf(p, (int)n);
+  return x < -126.f ? 0.f : r;
+}
+
 // s_waitcnt vmcnt(n) (n < 16) with expcnt and lgkmcnt left at their maxima.
 #define FA2_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
@@ -200,9 +219,12 @@ struct Args {
 //   KB : 32-key blocks per key tile  WPE: waves per SIMD the kernel is built for
 //   PIPE: software-pipelined main loop (see below)
 template <int NW_, int QB_, int KB_, int WPE_, int PIPE_ = 0, int LOOK_ = 0, int PRE_ = 0,
-          bool ASMDMA_ = false, int ASMPH_ = 0>
+          bool ASMDMA_ = false, int ASMPH_ = 0, int SWEXP_ = 0>
 struct Tile {
   static constexpr int NW = NW_, QB = QB_, KB = KB_, WPE = WPE_;
+  // SWEXP: the softmax's 2^x from sw_exp2 (FMA pipe) for every score (1), for
+  // every other score (2), or from v_exp_f32 only (0)
+  static constexpr int SWEXP = SWEXP_;
   // ASMPH (direct-copy loops, d = 128, 32 rows per wave, 64-key tiles):
   // issue each MFMA phase of a tile (16 score MFMAs; 16 P.V MFMAs) as one
   // inline-assembly block that keeps ASMPH MFMAs' worth of LDS operand
@@ -475,7 +497,14 @@ void fa2_fwd_kernel(Args a) {
           float p[8];
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * st + t], cc, -m_use));
+            const float x = __builtin_fmaf(s[qb][kb][8 * st + t], cc, -m_use);
+            if constexpr (TL::SWEXP == 1) {
+              p[t] = sw_exp2(x);
+            } else if constexpr (TL::SWEXP == 2) {
+              p[t] = (t & 1) ? sw_exp2(x) : __builtin_amdgcn_exp2f(x);
+            } else {
+              p[t] = __builtin_amdgcn_exp2f(x);
+            }
             if (t & 1) rs1 += p[t]; else rs0 += p[t];
           }
 #pragma unroll
