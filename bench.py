@@ -82,6 +82,22 @@ def time_gpu(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps, wall / steps * 1e3
 
 
+def per_call_stats(fn, calls: int):
+    """Per-call durations (ms) from one HIP event pair per call on the current
+    stream, taken after the timed region (they do not enter `value`)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"calls": calls, "median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5),
+            "p90_ms": round(t[min(len(t) - 1, int(0.9 * len(t)))], 5)}
+
+
 def cpu_baseline(w, budget_s: float = 20.0):
     """The fp64 CPU oracle timed on whole heads of the same workload (in order)
     until about budget_s seconds of work are done or every head is done."""
@@ -186,11 +202,14 @@ def run_backward(w, steps, warmup, variant=0):
         fa2.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, variant=variant, dq=dq, dk=dk, dv=dv,
                      delta=delta)
 
-    return time_gpu(step, steps, warmup)
+    res = time_gpu(step, steps, warmup)
+    run_backward.last_stats = per_call_stats(step, steps)
+    return res
 
 
 def backward_main(args, w):
     ms, wall_ms = run_backward(w, args.steps, args.warmup, args.variant)
+    stats = run_backward.last_stats
     peak = PEAK_TFLOPS[w.dtype]
     tflops = w.bwd_flops / (ms * 1e-3) / 1e12
     if args.all:
@@ -216,7 +235,7 @@ def backward_main(args, w):
         "data": "synthetic (seeded N(0,1) inputs and dO, rounded to the dtype)",
         "config": {**w.describe(), "pass": "backward (D, dK/dV, dQ kernels)", "variant": args.variant,
                    "parallelism": "single GPU",
-                   "wall_ms_per_step": round(wall_ms, 5)},
+                   "wall_ms_per_step": round(wall_ms, 5), "per_call": stats},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -244,6 +263,7 @@ def run_workload(w, steps, warmup, variant=0):
         fa2.forward(q, k, v, causal=w.causal, scale=w.scale, variant=variant, out=o, lse=lse)
 
     ms, wall_ms = time_gpu(step, steps, warmup)
+    run_workload.last_stats = per_call_stats(step, steps)
     return ms, wall_ms
 
 
@@ -293,6 +313,7 @@ def main():
         backward_main(args, w)
         return
     ms, wall_ms = run_workload(w, args.steps, args.warmup, args.variant)
+    stats = run_workload.last_stats
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = measured_traffic(w, args.variant)
@@ -319,7 +340,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs, rounded to the dtype)",
         "config": {**w.describe(), "variant": args.variant, "parallelism": "single GPU",
-                   "wall_ms_per_step": round(wall_ms, 5)},
+                   "wall_ms_per_step": round(wall_ms, 5), "per_call": stats},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
