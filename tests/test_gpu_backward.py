@@ -139,6 +139,17 @@ def test_backward_workload(name, heads):
     dq, dk, dv, delta = fa2.backward(qd, kd, vd, o, lse, do.cuda(), causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     check_heads(name, q, k, v, o_r, do, (dq, dk, dv, delta), w.causal, w.scale, w.dtype, heads)
+    # every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold exactly (causal or not); the
+    # allowance is the rounding of each summed element (4u of the sum of magnitudes) plus 1e-3
+    u = UNIT[w.dtype]
+    dk64, dv64, do64 = to_f64(dk), to_f64(dv), to_f64(do)
+    sk = np.abs(dk64.sum(axis=2))
+    sv = np.abs(dv64.sum(axis=2) - do64.sum(axis=2))
+    tol_k = 4 * u * np.abs(dk64).sum(axis=2) + 1e-3
+    tol_v = 4 * u * (np.abs(dv64).sum(axis=2) + np.abs(do64).sum(axis=2)) + 1e-3
+    print(f"{name} all heads: max|sum dK|/tol={(sk / tol_k).max():.3f}, "
+          f"max|sum dV - sum dO|/tol={(sv / tol_v).max():.3f}", flush=True)
+    assert np.all(sk <= tol_k) and np.all(sv <= tol_v)
 
 
 # ------------------------------------------------------------ properties
