@@ -12,7 +12,8 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_t dO_it O_it,
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three kernels, all enqueued on the caller's stream:
+// Three kernels, all enqueued on the caller's stream (two when the dQ kernel
+// computes D itself, FUSED_D):
 //   * fa2_bwd_delta_kernel: D_i = dO_i . O_i (fp32), one row per 8 or 16
 //     lanes, written to the caller's delta buffer;
 //   * dK/dV: one workgroup per (key block, head); 32 keys per wave or per
@@ -26,7 +27,9 @@
 //     LDS, so every product is computed once);
 //   * fa2_bwd_dq_kernel: one workgroup per (query block, head); each wave
 //     owns 32 queries, keeps their Q and dO rows in VGPRs and the dQ^T
-//     accumulator in registers, and walks the key tiles (K, V in LDS).
+//     accumulator in registers, and walks the key tiles (K, V in LDS);
+//     options: a copy ring (RING), a fixed MFMA issue order (LOOK), D
+//     computed in the kernel (FUSED_D).
 // dQ is thus produced by its own partition of the work, not by atomic adds
 // across key blocks: the result is deterministic and needs no workspace, at
 // the cost of recomputing S and dP in the dQ kernel.
