@@ -145,7 +145,8 @@ int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, co
  *
  * Every pointer is 16-byte aligned and owned by the caller; no output may
  * overlap an input or another output.  The call enqueues three kernels on
- * stream (D, then dK and dV, then dQ) and allocates nothing: dQ is computed
+ * stream (D, then dK and dV, then dQ; variant 10 of fa2_bwd_variant enqueues
+ * two: dQ, which also computes D, then dK and dV) and allocates nothing: dQ is computed
  * by its own kernel over query blocks instead of by atomic adds across key
  * blocks, so results are deterministic.  Validation and error codes as for
  * fa2_fwd (NULL, shape, d, alignment, overlap, argument), before any HIP
