@@ -207,6 +207,7 @@ struct BwdKernels {
   bwd_fn dkdv_pair_look[2][2][2];
   bwd_fn dkdv_pair_look2[2][2][2];
   bwd_fn dkdv_pair_look6[2][2][2];
+  bwd_fn dkdv_pipe[2][2][2];
   bwd_fn dq[2][2][2];
   bwd_fn dq_ring[2][2][2];
   bwd_fn dq_look[2][2][2];
@@ -235,6 +236,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_pair_look2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 2>;
   t.dkdv_pair_look6[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 6>;
   t.dkdv_pair_look6[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 6>;
+  t.dkdv_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, false, 4>;
+  t.dkdv_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, true, 4>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
@@ -275,8 +278,9 @@ const BwdKernels kBwd = make_bwd_kernels();
 // 10 = variant 9 with D computed by the dQ kernel, which runs first (two
 // launches instead of three); 11 = variant 1 with 4-wave (128-query) dQ
 // workgroups, MFMAs 4 operand reads ahead (at d = 128 it runs variant 1's
-// dQ kernel); 12, 13 = variant 9 with 2 and 6 operand reads ahead
-constexpr int kNumBwdVariants = 14;
+// dQ kernel); 12, 13 = variant 9 with 2 and 6 operand reads ahead; 14 =
+// the P hand-off pipelined across query tiles (one barrier per iteration)
+constexpr int kNumBwdVariants = 15;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
@@ -288,19 +292,21 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d",
                                                        "dkdv_w4_occ1_dq_w4_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look2_dq_look2",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6"};
+                                                       "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6",
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
-// d = 128 the P hand-off between the two waves of a SIMD with every MFMA
-// phase issued 4 operand reads ahead is fastest (headline shape 2.345 ms per
-// call against 2.375-2.385 with the order in the dQ kernel only, 2.41-2.42
-// with neither, 2.42-2.45 for the role split with 64-query tiles, 2.71 with
-// 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
+// d = 128 the P hand-off between the two waves of a SIMD pipelined across
+// query tiles is fastest (headline shape 2.23-2.24 ms per call against
+// 2.35-2.40 for the unpipelined hand-off with the same operand order,
+// N = 16384 causal 8.5-8.6 against 9.4 ms; earlier steps: 2.41-2.42 without
+// the operand order, 2.42-2.45 for the role split with 64-query tiles, 2.71
+// with 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
 // against 0.130-0.133 for variants 6, 7 and 11), and for causal d = 64
 // variant 11, whose 4-wave dQ workgroups balance the triangular work
 // (0.095 against 0.103 ms).
 int default_bwd_variant(int d, int causal) {
-  if (d == 128) return 9;
+  if (d == 128) return 14;
   return causal ? 11 : 1;
 }
 
@@ -378,7 +384,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
     }
     a.nblk = (N + QTile::BR - 1) / QTile::BR;
     bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
-                 : (vi == 8 || vi == 9) ? kBwd.dq_look[bf16][big][causal]
+                 : (vi == 8 || vi == 9 || vi == 14) ? kBwd.dq_look[bf16][big][causal]
                  : vi == 10             ? kBwd.dq_look_fused[bf16][big][causal]
                  : vi == 12             ? kBwd.dq_look2[bf16][big][causal]
                  : vi == 13             ? kBwd.dq_look6[bf16][big][causal]
@@ -400,7 +406,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   }
 
   if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10 || vi == 12 ||
-      vi == 13) {
+      vi == 13 || vi == 14) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
@@ -408,6 +414,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
               : (vi == 9 || vi == 10) ? kBwd.dkdv_pair_look[bf16][big][causal]
               : vi == 12 ? kBwd.dkdv_pair_look2[bf16][big][causal]
               : vi == 13 ? kBwd.dkdv_pair_look6[bf16][big][causal]
+              : vi == 14 ? kBwd.dkdv_pipe[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {

@@ -955,6 +955,266 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV with the P hand-off pipelined across query tiles: the layout of
+// fa2_bwd_dkdv_pair_kernel (8 waves, wave w and w+4 own keys
+// [k_wg + 32*(w%4), +32), 64-query tiles of two 32-query sub-blocks), with
+// one barrier per iteration.  In iteration t:
+//   dV wave: dV^T += dO^T P of tile t-1 (P kept packed in registers), then
+//            S and P of tile t, P stored packed (16-bit) in LDS slot t % 2;
+//   dK wave: P of tile t-1 from slot (t-1) % 2, dS = P (dP - D) with the dP
+//            of tile t-1 kept in registers, dK^T += Q^T dS, then dP of tile t.
+// Both waves start every iteration with MFMAs that need nothing from the
+// other, and each one's VALU work meets the other's MFMAs.  The query tiles
+// t-1, t and t+1 are in a 3-stage LDS ring (tile t+1 copied at the start of
+// iteration t).  dS is formed from the 16-bit P (its rounding adds at most
+// half a unit of the dtype to dS).
+template <bool BF16, int D, bool CAUSAL, int LOOK = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv_pipe_kernel(BwdArgs a) {
+  using E = Elem<BF16>;
+  constexpr int BK = 128;
+  constexpr int SUB = 2;
+  constexpr int BQ = 32 * SUB;
+  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
+  constexpr int TSZ = BQ * KROW;
+  constexpr int STAGE = 2 * TSZ + 2 * 64 * 4;
+  constexpr int NS = 3;
+  constexpr int PSUB = 64 * 32;             // packed P of one sub-block of one key group: 32 bytes per lane
+  constexpr int PPAR = SUB * PSUB;          // ... of one tile
+  constexpr int PBASE = NS * STAGE;
+  constexpr int SMEM = PBASE + 4 * 2 * PPAR;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int grp = wave & 3;
+  const bool dk_role = __builtin_amdgcn_readfirstlane(wave) >= 4;
+
+  int bh, kblk;
+  {
+    const int i = blockIdx.x;
+    const int total = a.nblk * a.BH;
+    if constexpr (!CAUSAL) {
+      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+      bh = logical / a.nblk;
+      kblk = logical % a.nblk;
+    } else {
+      bh = i % a.BH;
+      kblk = i / a.BH;
+    }
+  }
+  const int N = a.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  auto rsrc = [&](const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
+  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+
+  const int k_wg = kblk * BK;
+  const int k_w = k_wg + 32 * grp;
+  const int key = k_w + lr;
+
+  // the dV wave keeps the group's K rows (for S), the dK wave its V rows (for dP)
+  u32x4 bf[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk)
+    bf[dk] = __builtin_amdgcn_raw_buffer_load_b128(dk_role ? vr : kr, (uint32_t)(key * KROW + (2 * dk + lh) * 16), 0, 0);
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  const int nt = (N + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? k_wg / BQ : 0;
+
+  const FragAddr<D> fa(lane);
+  const float c = a.c;
+  // this lane's packed P of (key group, parity, sub-block): 2 x 16 bytes, lane-contiguous
+  uint8_t* const pslot = smem + PBASE + grp * 2 * PPAR + 16 * lane;
+
+  auto sub_skip = [&](int q0) { return CAUSAL && q0 + 31 < k_w; };
+  auto sub_masked = [&](int q0) { return (q0 + 32 > N) || (CAUSAL && q0 < k_w + 31); };
+  auto order_fread = [&]() {
+    if constexpr (LOOK > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < DK - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    }
+  };
+  auto order_tread = [&]() {
+    if constexpr (LOOK > 0) {
+      constexpr int NM = 2 * DB;
+      constexpr int LA = LOOK < NM ? LOOK : NM;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LA, 0);
+#pragma unroll
+      for (int i = 0; i < NM - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LA, 0);
+    }
+  };
+
+  u32x4 pk[SUB][2];     // dV wave: packed P of the previous tile
+  f32x16 dp[SUB];       // dK wave: dP of the previous tile
+#pragma unroll
+  for (int sb = 0; sb < SUB; ++sb) {
+    pk[sb][0] = u32x4{};
+    pk[sb][1] = u32x4{};
+    dp[sb] = f32x16{};
+  }
+
+  // tail of tile t (stage st): dV^T += dO^T P (dV wave), or dS and dK^T += Q^T dS (dK wave)
+  auto tail = [&](const uint8_t* st, int t) {
+    const uint8_t* qt = st;
+    const uint8_t* dot = st + TSZ;
+    const float* dl = (const float*)(st + 2 * TSZ) + 64;
+    const uint8_t* ps = pslot + (t & 1) * PPAR;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int q0 = t * BQ + 32 * sb;
+      if (sub_skip(q0)) continue;
+      if (!dk_role) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(dot, 32 * sb + 16 * h, db), pk[sb][h], acc[db]);
+        order_tread();
+      } else {
+        u32x4 ds[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 pw = *(const u32x4*)(ps + sb * PSUB + h * 1024);
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const int r = 8 * h + 2 * t2;          // registers r, r+1: queries of group r/4
+            const f32x4 dq4 = *(const f32x4*)(dl + 32 * sb + 8 * (r >> 2) + 4 * lh);
+            const float v0 = half_lo<BF16>(pw[t2]) * (dp[sb][r] - dq4[r & 3]);
+            const float v1 = half_hi<BF16>(pw[t2]) * (dp[sb][r + 1] - dq4[(r + 1) & 3]);
+            ds[h][t2] = E::pack(v0, v1);
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(qt, 32 * sb + 16 * h, db), ds[h], acc[db]);
+      }
+    }
+  };
+  // head of tile t (stage st): S and packed P to registers and LDS (dV wave), or dP (dK wave)
+  auto head = [&](const uint8_t* st, int t) {
+    const uint8_t* qt = st;
+    const uint8_t* dot = st + TSZ;
+    const float* l2 = (const float*)(st + 2 * TSZ);
+    uint8_t* ps = pslot + (t & 1) * PPAR;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int q0 = t * BQ + 32 * sb;
+      if (sub_skip(q0)) continue;
+      if (!dk_role) {
+        f32x16 sv = f32x16{};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) sv = E::mfma(fa.fread(qt, 32 * sb, dk), bf[dk], sv);
+        order_fread();
+        const bool masked = sub_masked(q0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lq = *(const f32x4*)(l2 + 32 * sb + 8 * g + 4 * lh) * kLog2e;
+          float pv[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * g + b], c, -lq[b]));
+            if (masked) {
+              const int q = q0 + 8 * g + 4 * lh + b;
+              x = (q < N && (!CAUSAL || key <= q)) ? x : 0.f;
+            }
+            pv[b] = x;
+          }
+          pk[sb][g >> 1][2 * (g & 1)] = E::pack(pv[0], pv[1]);
+          pk[sb][g >> 1][2 * (g & 1) + 1] = E::pack(pv[2], pv[3]);
+        }
+        *(u32x4*)(ps + sb * PSUB) = pk[sb][0];
+        *(u32x4*)(ps + sb * PSUB + 1024) = pk[sb][1];
+      } else {
+        f32x16 d = f32x16{};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) d = E::mfma(fa.fread(dot, 32 * sb, dk), bf[dk], d);
+        order_fread();
+        dp[sb] = d;
+      }
+    }
+  };
+
+  // ---- 3-stage ring: tiles t-1, t, t+1 -----------------------------------------
+  constexpr int NI = TSZ / 1024;
+  constexpr int IPW = 2 * NI / 8;
+  static_assert(2 * NI % 8 == 0 && IPW >= 1 && IPW + 1 < 16, "tile copies must split evenly over the waves");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dsrc[IPW];
+  int ddst[IPW];
+  bool dq_t[IPW];
+#pragma unroll
+  for (int k = 0; k < IPW; ++k) {
+    const int i = wv * IPW + k;
+    dq_t[k] = i >= NI;
+    const int b = (i % NI) * 1024 + 16 * lane;
+    const int row = b / KROW, phys = (b % KROW) / 16;
+    dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+    ddst[k] = (dq_t[k] ? TSZ : 0) + (i % NI) * 1024;
+  }
+  const bool stat_wave = wv < 2;
+  auto dma = [&](int t, int stg) {
+    uint8_t* base = smem + stg * STAGE;
+    const int qoff = t * BQ * KROW;
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k], qoff);
+    if (stat_wave) lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * lane), t * BQ * 4);
+  };
+  if (t0 < nt) {
+    dma(t0, 0);
+    // the fragment loads and tile t0 have landed (see the split kernel for the empty statement)
+    FA2_WAIT_VMCNT(0);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(bf[dk]));
+    __syncthreads();
+    for (int t = t0; t <= nt; ++t) {
+      const int i = t - t0;
+      // stage (i+1)%3 held tile t-2, last used in iteration t-1
+      if (t + 1 < nt) dma(t + 1, (i + 1) % 3);
+      if (t > t0) tail(smem + ((i + 2) % 3) * STAGE, t - 1);
+      if (t < nt) head(smem + (i % 3) * STAGE, t);
+      // tile t+1 (this iteration's copies) must have landed for iteration t+1
+      FA2_WAIT_VMCNT(0);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: dV = dV^T or dK = scale * dK^T, transposed back ----------
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)(dk_role ? a.dk : a.dv) + head_off), 0, head_bytes, kBufferWord3);
+  const float sc = dk_role ? a.scale : 1.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * lh;
+      u32x2 w;
+      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
+      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
+      __builtin_amdgcn_raw_buffer_store_b64(w, outr, (uint32_t)(key * KROW + d * 2), 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per (query block of 32*NW queries, head), wave w owns
 // queries [q_wg + 32w, +32).  Key tiles of 64 rows: K and V (row-major,
 // swizzled) staged in LDS.  RING = false: two stages, register-staged copies

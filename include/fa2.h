@@ -195,8 +195,11 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *   11 "dkdv_w4_occ1_dq_w4_look4": variant 1 with 4-wave (128-query) dQ
  *     workgroups at d = 64 (twice the workgroups for small grids); at
  *     d = 128 it is variant 1;
- *   12, 13: variant 9 with 2 and 6 operand reads ahead instead of 4.
- * The default is variant 9 for d = 128, variant 1 for non-causal d = 64 and
+ *   12, 13: variant 9 with 2 and 6 operand reads ahead instead of 4;
+ *   14 "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4": the P hand-off
+ *     pipelined across query tiles, one barrier per iteration (P passed as
+ *     16-bit values).
+ * The default is variant 14 for d = 128, variant 1 for non-causal d = 64 and
  * variant 11 for causal d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */

@@ -5,8 +5,9 @@ oracle is within a bound derived from the rounding the kernels perform.  Two
 properties make that bound meaningful, and both are checked here without a
 GPU:
   * it is not too tight: a NumPy model of the kernels' arithmetic (P from the
-    saved fp32 LSE, P and dS rounded to the input dtype, D from the O stored
-    in the dtype, outputs rounded to the dtype) stays inside it;
+    saved fp32 LSE, P and dS rounded to the input dtype, dS formed from the
+    fp32 or from the rounded P, D from the O stored in the dtype, outputs
+    rounded to the dtype) stays inside it;
   * it is not vacuous: plausible kernel mistakes (D dropped, dS without the
     factor P, scale dropped, causal mask dropped, a product not transposed,
     the LSE taken in the wrong base) land outside it for some element.
@@ -35,8 +36,9 @@ def f32(x):
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
-def kernel_model(q, k, v, o_r, lse32, do, causal, scale, dtype, mistake=None):
-    """The kernels' arithmetic for one head, optionally with one planted mistake."""
+def kernel_model(q, k, v, o_r, lse32, do, causal, scale, dtype, mistake=None, p16_in_ds=False):
+    """The kernels' arithmetic for one head, optionally with one planted mistake.
+    p16_in_ds: dS formed from the 16-bit P (the pipelined dK/dV kernel) instead of the fp32 P."""
     n = q.shape[0]
     vis = oracle.visible_mask(np.arange(n), n, causal)
     if mistake == "unmasked_p":
@@ -49,7 +51,8 @@ def kernel_model(q, k, v, o_r, lse32, do, causal, scale, dtype, mistake=None):
     delta = f32((do * o_r).sum(axis=1))
     if mistake == "no_delta":
         delta = np.zeros_like(delta)
-    ds = f32(dp - delta[:, None]) if mistake == "ds_without_p" else f32(p * (dp - delta[:, None]))
+    p_ds = rnd(p, dtype) if p16_in_ds else p
+    ds = f32(dp - delta[:, None]) if mistake == "ds_without_p" else f32(p_ds * (dp - delta[:, None]))
     ds_r = rnd(ds, dtype)
     sq = 1.0 if mistake == "dq_no_scale" else scale
     dq = rnd(sq * (ds_r @ k), dtype)
@@ -71,13 +74,14 @@ def case(dtype, causal, seed, n=96, d=64):
     return q, k, v, o_r, lse32, do, scale, ref, bounds
 
 
+@pytest.mark.parametrize("p16_in_ds", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_kernel_rounding_stays_inside_the_bound(dtype, causal):
+def test_kernel_rounding_stays_inside_the_bound(dtype, causal, p16_in_ds):
     q, k, v, o_r, lse32, do, scale, ref, bounds = case(dtype, causal, seed=101)
-    got = kernel_model(q, k, v, o_r, lse32, do, causal, scale, dtype)
+    got = kernel_model(q, k, v, o_r, lse32, do, causal, scale, dtype, p16_in_ds=p16_in_ds)
     ratios = [worst_ratio(g, r, b) for g, r, b in zip(got, ref, bounds)]
-    print(dtype, causal, ["%.3f" % x for x in ratios])
+    print(dtype, causal, p16_in_ds, ["%.3f" % x for x in ratios])
     assert max(ratios) <= 1.0, ratios
 
 
