@@ -214,6 +214,7 @@ struct BwdKernels {
   bwd_fn dq_look2[2][2][2];
   bwd_fn dq_look6[2][2][2];
   bwd_fn dq_look_fused[2][2][2];
+  bwd_fn dq_pipe[2][2][2];
   bwd_fn dq4_look[2][2];       // [bf16][causal], d = 64 only
 };
 
@@ -250,6 +251,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dq_look6[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 6>;
   t.dq_look_fused[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4, true>;
   t.dq_look_fused[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4, true>;
+  t.dq_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dq_pipe_kernel<BF16, D, false, 4>;
+  t.dq_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dq_pipe_kernel<BF16, D, true, 4>;
 }
 
 BwdKernels make_bwd_kernels() {
@@ -280,7 +283,7 @@ const BwdKernels kBwd = make_bwd_kernels();
 // workgroups, MFMAs 4 operand reads ahead (at d = 128 it runs variant 1's
 // dQ kernel); 12, 13 = variant 9 with 2 and 6 operand reads ahead; 14 =
 // the P hand-off pipelined across query tiles (one barrier per iteration)
-constexpr int kNumBwdVariants = 15;
+constexpr int kNumBwdVariants = 16;
 const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
                                                        "dkdv_w8_split_occ2_ring4",
                                                        "dkdv_w8_split_occ2_ring4_dq_ring3",
@@ -293,7 +296,8 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w4_occ1_dq_w4_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look2_dq_look2",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6",
-                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4"};
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4",
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_pipe_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD pipelined across
@@ -388,6 +392,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
                  : vi == 10             ? kBwd.dq_look_fused[bf16][big][causal]
                  : vi == 12             ? kBwd.dq_look2[bf16][big][causal]
                  : vi == 13             ? kBwd.dq_look6[bf16][big][causal]
+                 : vi == 15             ? kBwd.dq_pipe[bf16][big][causal]
                                         : kBwd.dq[bf16][big][causal];
     hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
     return hipGetLastError() == hipSuccess;
@@ -406,7 +411,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   }
 
   if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10 || vi == 12 ||
-      vi == 13 || vi == 14) {
+      vi == 13 || vi == 14 || vi == 15) {
     a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
     bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
               : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
@@ -414,7 +419,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
               : (vi == 9 || vi == 10) ? kBwd.dkdv_pair_look[bf16][big][causal]
               : vi == 12 ? kBwd.dkdv_pair_look2[bf16][big][causal]
               : vi == 13 ? kBwd.dkdv_pair_look6[bf16][big][causal]
-              : vi == 14 ? kBwd.dkdv_pipe[bf16][big][causal]
+              : (vi == 14 || vi == 15) ? kBwd.dkdv_pipe[bf16][big][causal]
                         : kBwd.dkdv_ring[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {

@@ -1496,4 +1496,218 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ pipelined across key tiles: the layout of fa2_bwd_dq_kernel (8 waves x
+// 32 queries, 64-key tiles), with the dQ^T += K^T dS^T product of tile j-1
+// issued at the start of iteration j from the packed dS^T kept in registers,
+// before the S^T and dP^T products of tile j, so each wave starts every
+// iteration with MFMAs that do not wait for that iteration's scores.  K and V
+// tiles j-1 .. j+2 are in a 4-stage LDS ring filled by inline-assembly copies
+// (tile j+2 issued at the start of iteration j, two tiles in flight); one
+// barrier per iteration.
+template <bool BF16, int D, bool CAUSAL, int LOOK = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dq_pipe_kernel(BwdArgs a) {
+  using E = Elem<BF16>;
+  constexpr int NW = 8, BR = 32 * NW;
+  constexpr int BC = 64;
+  constexpr int NKB = BC / 32;
+  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
+  constexpr int TSZ = BC * KROW;
+  constexpr int STAGE = 2 * TSZ;
+  constexpr int NS = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  int bh, qblk;
+  {
+    const int i = blockIdx.x;
+    const int total = a.nblk * a.BH;
+    if constexpr (!CAUSAL) {
+      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+      bh = logical / a.nblk;
+      qblk = logical % a.nblk;
+    } else {
+      bh = i % a.BH;
+      qblk = a.nblk - 1 - i / a.BH;
+    }
+  }
+  const int N = a.N;
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  auto rsrc = [&](const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
+  };
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
+
+  const int q_wg = qblk * BR;
+  const int q_w = q_wg + 32 * wave;
+  const int q = q_w + lr;
+
+  u32x4 qf[DK], dof[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    const uint32_t off = (uint32_t)(q * KROW + (2 * dk + lh) * 16);
+    qf[dk] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
+    dof[dk] = __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+  const float lse2 =
+      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lser, (uint32_t)(q * 4), 0, 0)) * kLog2e;
+  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  int nt = (N + BC - 1) / BC;
+  if constexpr (CAUSAL) {
+    const int last_row = min(q_wg + BR, N) - 1;
+    nt = min(nt, last_row / BC + 1);
+  }
+  auto tile_skip = [&](int key0) { return CAUSAL && key0 > q_w + 31; };
+
+  const FragAddr<D> fa(lane);
+  const float c = a.c;
+  u32x4 dsp[NKB][2];    // packed dS^T of the previous tile
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    dsp[kb][0] = u32x4{};
+    dsp[kb][1] = u32x4{};
+  }
+
+  // tail of tile j (stage st): dQ^T += K^T dS^T
+  auto tail = [&](const uint8_t* st) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(st, 32 * kb + 16 * h, db), dsp[kb][h], acc[db]);
+    if constexpr (LOOK > 0) {
+      constexpr int NM = DB * NKB * 2;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < NM - LOOK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LOOK, 0);
+    }
+  };
+  // head of tile j (stage st): S^T, dP^T, then dS^T packed into dsp
+  auto head = [&](const uint8_t* st, int key0) {
+    const uint8_t* kt = st;
+    const uint8_t* vt = st + TSZ;
+    const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
+    f32x16 sv[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sv[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sv[kb] = E::mfma(fa.fread(kt, 32 * kb, dk), qf[dk], sv[kb]);
+        dp[kb] = E::mfma(fa.fread(vt, 32 * kb, dk), dof[dk], dp[kb]);
+      }
+    }
+    if constexpr (LOOK > 0) {
+      constexpr int NM = 2 * NKB * DK;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < NM - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c, -lse2));
+        if (masked) {
+          const int kk = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool vis = kk < N && (!CAUSAL || kk <= q);
+          pv = vis ? pv : 0.f;
+        }
+        ds[r] = pv * (dp[kb][r] - dlt);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dsp[kb][h][t] = E::pack(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
+    }
+  };
+
+  // ---- 4-stage ring: K, V tiles j-1 .. j+2 -----------------------------------
+  constexpr int NI = TSZ / 1024;
+  constexpr int IPW = 2 * NI / NW;
+  static_assert(2 * NI % NW == 0 && IPW >= 1 && 2 * IPW < 16, "tile copies must split evenly over the waves");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dsrc[IPW];
+  int ddst[IPW];
+  bool isv[IPW];
+#pragma unroll
+  for (int k = 0; k < IPW; ++k) {
+    const int i = wv * IPW + k;
+    isv[k] = i >= NI;
+    const int b = (i % NI) * 1024 + 16 * lane;
+    const int row = b / KROW, phys = (b % KROW) / 16;
+    dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
+    ddst[k] = (isv[k] ? TSZ : 0) + (i % NI) * 1024;
+  }
+  auto dma = [&](int j, int stg) {
+    uint8_t* base = smem + stg * STAGE;
+    const int koff = j * BC * KROW;
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) lds_dma16_asm(isv[k] ? vr : kr, base + ddst[k], dsrc[k], koff);
+  };
+  dma(0, 0);
+  if (nt > 1) dma(1, 1);
+  // Q, dO fragments, LSE, D (loaded before the copies) and tile 0 have landed
+  // once at most tile 1's copies remain
+  if (nt > 1) FA2_WAIT_VMCNT(IPW);
+  else FA2_WAIT_VMCNT(0);
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(qf[dk]), "v"(dof[dk]));
+  asm volatile("" ::"v"(lse2), "v"(dlt));
+  __syncthreads();
+  for (int j = 0; j <= nt; ++j) {
+    // stage (j+2)%4 held tile j-2, last used in iteration j-1
+    if (j + 2 < nt) dma(j + 2, (j + 2) % 4);
+    if (j >= 1 && !tile_skip((j - 1) * BC)) tail(smem + ((j + 3) % 4) * STAGE);
+    if (j < nt && !tile_skip(j * BC)) head(smem + (j % 4) * STAGE, j * BC);
+    // tile j+1 (issued one iteration earlier) must have landed for iteration
+    // j+1; tile j+2's copies may remain
+    if (j + 2 < nt) FA2_WAIT_VMCNT(IPW);
+    else FA2_WAIT_VMCNT(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T (transposed back) ----------------------
+  const __amdgpu_buffer_rsrc_t dqr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)a.dq + head_off), 0, head_bytes, kBufferWord3);
+  const float sc = a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * lh;
+      u32x2 w;
+      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
+      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
+      __builtin_amdgcn_raw_buffer_store_b64(w, dqr, (uint32_t)(q * KROW + d * 2), 0, 0);
+    }
+  }
+}
+
 }  // namespace fa2

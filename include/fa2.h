@@ -199,6 +199,9 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *   14 "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4": the P hand-off
  *     pipelined across query tiles, one barrier per iteration (P passed as
  *     16-bit values).
+ *   15 "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_pipe_look4": variant 14 with
+ *     the dQ kernel pipelined across key tiles too (dQ of tile j-1 from
+ *     dS kept in registers, then S, dP, dS of tile j; 4-stage K/V ring).
  * The default is variant 14 for d = 128, variant 1 for non-causal d = 64 and
  * variant 11 for causal d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
