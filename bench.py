@@ -132,15 +132,19 @@ API_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_api.hip")
 
 def bwd_identity(w) -> str:
     """Hash of the backward kernel source (without its // comments, whitespace
-    collapsed), the host function that picks the default backward
-    configuration, and dtype/d/causal."""
+    collapsed), the host table that instantiates the backward kernels with
+    their template arguments, the host function that picks the default
+    backward configuration, and dtype/d/causal."""
     import re
     h = hashlib.sha256()
     with open(BWD_KERNEL_SOURCE) as f:
         h.update(" ".join(re.sub(r"//[^\n]*", "", f.read()).split()).encode())
     with open(API_SOURCE) as f:
-        m = re.search(r"int default_bwd_variant\(.*?\n}", f.read(), flags=re.S)
-    h.update((m.group(0) if m else "").encode())
+        api = f.read()
+    for pat in (r"constexpr void fill_bwd\(.*?\n}", r"BwdKernels make_bwd_kernels\(.*?\n}",
+                r"int default_bwd_variant\(.*?\n}"):
+        m = re.search(pat, api, flags=re.S)
+        h.update((m.group(0) if m else "").encode())
     h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
     return h.hexdigest()[:16]
 

@@ -237,8 +237,8 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.dkdv_pair_look2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 2>;
   t.dkdv_pair_look6[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 6>;
   t.dkdv_pair_look6[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 6>;
-  t.dkdv_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, false, 4>;
-  t.dkdv_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, true, 4>;
+  t.dkdv_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, false, 2>;
+  t.dkdv_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, true, 2>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
   t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
@@ -296,8 +296,8 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w4_occ1_dq_w4_look4",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look2_dq_look2",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6",
-                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4",
-                                                       "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_pipe_look4"};
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4",
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_pipe_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD pipelined across

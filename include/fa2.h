@@ -196,10 +196,10 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *     workgroups at d = 64 (twice the workgroups for small grids); at
  *     d = 128 it is variant 1;
  *   12, 13: variant 9 with 2 and 6 operand reads ahead instead of 4;
- *   14 "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_look4": the P hand-off
+ *   14 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4": the P hand-off
  *     pipelined across query tiles, one barrier per iteration (P passed as
- *     16-bit values).
- *   15 "dkdv_w8_pipe_occ2_ring3_q64_look4_dq_pipe_look4": variant 14 with
+ *     16-bit values, dK/dV MFMAs two operand reads ahead).
+ *   15 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_pipe_look4": variant 14 with
  *     the dQ kernel pipelined across key tiles too (dQ of tile j-1 from
  *     dS kept in registers, then S, dP, dS of tile j; 4-stage K/V ring).
  * The default is variant 14 for d = 128, variant 1 for non-causal d = 64 and
