@@ -13,6 +13,7 @@
 #include "fa2_fwd_kernel.hpp"
 #include "fa2_bwd_kernel.hpp"
 #include "fa2_fwd_roles.hpp"
+#include "fa2_fwd_sched.hpp"
 
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -53,6 +54,19 @@ constexpr Variant make_roles_variant(const char* name) {
                    {fa2::fa2_fwd_roles_kernel<true, 128, false>, fa2::fa2_fwd_roles_kernel<true, 128, true>}}}};
 }
 
+// The scheduled kernel (fa2_fwd_sched.hpp) at d = 128; d = 64 runs the
+// 128-key-tile kernel of the same workgroup shape (8 waves, 256 rows).
+constexpr Variant make_sched_variant(const char* name) {
+  using D64 = Tile<8, 1, 4, 2, 5, 4>;
+  return Variant{name,
+                 512,
+                 fa2::kSchedRows,
+                 {{{fa2::fa2_fwd_kernel<false, 64, false, D64>, fa2::fa2_fwd_kernel<false, 64, true, D64>},
+                   {fa2::fa2_fwd_sched_kernel<false, false>, fa2::fa2_fwd_sched_kernel<false, true>}},
+                  {{fa2::fa2_fwd_kernel<true, 64, false, D64>, fa2::fa2_fwd_kernel<true, 64, true, D64>},
+                   {fa2::fa2_fwd_sched_kernel<true, false>, fa2::fa2_fwd_sched_kernel<true, true>}}}};
+}
+
 // Index 0 is the tuned default; it is resolved per (dtype, d, causal) by
 // default_variant() below.
 const Variant kVariants[] = {
@@ -83,20 +97,22 @@ const Variant kVariants[] = {
     make_roles_variant("w8_pairs32_k64_roles_ring3"),  // softmax wave + P.V wave per SIMD, P through LDS
     make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 1>>("w8_q32_k64_dma3_look4_swexp"),      // variant 11, every 2^x in software
     make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 2>>("w8_q32_k64_dma3_look4_swexp_half"), // variant 11, every other 2^x in software
+    make_sched_variant("w8_q32_k64_sched_ring4"),   // hand-scheduled main loop, waves paired half a tile apart
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+static_assert(kNumVariants == 28, "variant table");
 
-// Measured on MI355X (bench.py, same box, each variant twice, alternating):
-// non-causal d = 128 is fastest with 64-key tiles in a 3-stage direct-copy
-// ring and 4 operand reads ahead (variant 11); causal d = 128 and
-// non-causal d = 64 with 128-key tiles in a 2-stage ring and 4 operand reads
-// ahead (variant 14); causal d = 64 with 4-wave workgroups, two per CU, on a
-// 2-stage ring of 64-key tiles (variant 10: twice the workgroups balance the
-// triangular work, and the two workgroups of a CU are not held in step by
-// one barrier).
+// Measured on MI355X (same box, alternating runs): d = 128, causal or not,
+// runs the hand-scheduled kernel (variant 27: headline shape 0.49-0.50 ms
+// per call against 0.52-0.53 for variant 11, N = 16384 causal 1.84 against
+// 1.88 ms, N = 4096 causal a tie); non-causal d = 64 runs 128-key tiles in a
+// 2-stage ring with 4 operand reads ahead (variant 14); causal d = 64 runs
+// 4-wave workgroups, two per CU, on a 2-stage ring of 64-key tiles (variant
+// 10: twice the workgroups balance the triangular work).
+constexpr int kSchedVariant = 27;
 int default_variant(int bf16, int d, int causal) {
   (void)bf16;
-  if (d == 128) return causal ? 14 : 11;
+  if (d == 128) return kSchedVariant;
   return causal ? 10 : 14;
 }
 
