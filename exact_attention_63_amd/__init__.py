@@ -129,6 +129,14 @@ def _dtype_code(dtype) -> int:
     raise ValueError(f"q, k, v must be float16 or bfloat16, got {dtype}")
 
 
+def _check_empty(d: int, variant: int, nvar: int) -> None:
+    """The library's argument checks that still apply to an empty problem."""
+    if not 0 <= int(variant) < nvar:
+        raise Fa2Error(FA2_ERR_ARG, "variant")
+    if d not in (64, 128):
+        raise Fa2Error(FA2_ERR_UNSUPPORTED, "head dimension")
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, *, variant: int = 0,
             out=None, lse=None):
     """Attention forward: returns (O [B,H,N,d] in q's dtype, LSE [B,H,N] float32).
@@ -136,7 +144,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
     q, k, v: contiguous CUDA (ROCm) tensors [B, H, N, d] of one dtype (fp16 or
     bf16), d in {64, 128}.  scale defaults to 1/sqrt(d).  The kernel is
     enqueued on the current stream of q's device; the call does not
-    synchronise.  ``out`` / ``lse`` may pass preallocated outputs.
+    synchronise.  ``out`` / ``lse`` may pass preallocated outputs.  An empty
+    problem (B, H or N == 0) returns the empty outputs without a library call
+    (the C ABI returns FA2_ERR_SHAPE for it).
     """
     import torch
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
@@ -164,6 +174,10 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    if out.numel() == 0:
+        # B, H or N is 0: nothing to compute (the library rejects empty sizes)
+        _check_empty(d, variant, num_variants())
+        return out, lse
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         rc = lib().fa2_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -228,6 +242,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous() \
             or delta.device != q.device:
         raise ValueError("delta must be a contiguous float32 tensor [B, H, N] on q's device")
+    if dq.numel() == 0:
+        _check_empty(d, variant, bwd_num_variants())
+        return dq, dk, dv, delta
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         rc = lib().fa2_bwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),

@@ -7,6 +7,8 @@
 // constant tables, and validates every argument before touching the HIP
 // runtime, so an invalid call has no effect.
 #include <stdint.h>
+#include <algorithm>
+#include <atomic>
 #include <string.h>
 
 #include "fa2.h"
@@ -30,6 +32,9 @@ struct Variant {
   int threads;
   int rows_per_block;     // BR
   kernel_fn fn[2][2][2];  // [bf16][d == 128][causal]
+  // persistent kernel for d = 128, non-causal, N % 256 == 0 (one workgroup
+  // per CU); null where the variant has none
+  kernel_fn persist[2];   // [bf16]
 };
 
 template <class TL>
@@ -64,7 +69,16 @@ constexpr Variant make_sched_variant(const char* name) {
                  {{{fa2::fa2_fwd_kernel<false, 64, false, D64>, fa2::fa2_fwd_kernel<false, 64, true, D64>},
                    {fa2::fa2_fwd_sched_kernel<false, false>, fa2::fa2_fwd_sched_kernel<false, true>}},
                   {{fa2::fa2_fwd_kernel<true, 64, false, D64>, fa2::fa2_fwd_kernel<true, 64, true, D64>},
-                   {fa2::fa2_fwd_sched_kernel<true, false>, fa2::fa2_fwd_sched_kernel<true, true>}}}};
+                   {fa2::fa2_fwd_sched_kernel<true, false>, fa2::fa2_fwd_sched_kernel<true, true>}}},
+                 {nullptr, nullptr}};
+}
+
+// ... with its persistent form where the shape allows it
+constexpr Variant make_sched_persist_variant(const char* name) {
+  Variant v = make_sched_variant(name);
+  v.persist[0] = fa2::fa2_fwd_sched_persist_kernel<false>;
+  v.persist[1] = fa2::fa2_fwd_sched_persist_kernel<true>;
+  return v;
 }
 
 // Index 0 is the tuned default; it is resolved per (dtype, d, causal) by
@@ -98,9 +112,10 @@ const Variant kVariants[] = {
     make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 1>>("w8_q32_k64_dma3_look4_swexp"),      // variant 11, every 2^x in software
     make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 2>>("w8_q32_k64_dma3_look4_swexp_half"), // variant 11, every other 2^x in software
     make_sched_variant("w8_q32_k64_sched_ring4"),   // hand-scheduled main loop, waves paired half a tile apart
+    make_sched_persist_variant("w8_q32_k64_sched_persist"),   // ... one workgroup per CU over the items
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-static_assert(kNumVariants == 28, "variant table");
+static_assert(kNumVariants == 29, "variant table");
 
 // Measured on MI355X (same box, alternating runs): d = 128, causal or not,
 // runs the hand-scheduled kernel (variant 27: headline shape 0.49-0.50 ms
@@ -116,6 +131,19 @@ int default_variant(int bf16, int d, int causal) {
   return causal ? 10 : 14;
 }
 
+// compute units of the current device (one persistent workgroup each)
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // finite test on the bit pattern (independent of floating-point compile flags)
 bool finite_bits(float x) {
   uint32_t u;
@@ -128,9 +156,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Validation shared by every entry point; FA2_OK means "launch", a positive
-// kEmpty means "valid and nothing to do".
-constexpr int kEmpty = 1;
+// Validation shared by every entry point; FA2_OK means "launch".
 
 int check(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
           int H, int N, int d, int causal, float scale, int dtype, int variant) {
@@ -138,8 +164,7 @@ int check(const void* q, const void* k, const void* v, const void* o, const void
   if (causal != 0 && causal != 1) return FA2_ERR_ARG;
   if (!finite_bits(scale)) return FA2_ERR_ARG;
   if (variant < 0 || variant >= kNumVariants) return FA2_ERR_ARG;
-  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
-  if (B == 0 || H == 0 || N == 0) return kEmpty;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
   if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
   // one head must be addressable with 32-bit byte offsets
@@ -165,7 +190,6 @@ int check(const void* q, const void* k, const void* v, const void* o, const void
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
         int d, int causal, float scale, hipStream_t stream, int dtype, int variant) {
   const int st = check(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, variant);
-  if (st == kEmpty) return FA2_OK;
   if (st != FA2_OK) return st;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
 
@@ -187,7 +211,12 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   a.c = scale * 1.4426950408889634f;  // scale * log2(e)
 
   kernel_fn fn = var.fn[bf16][d == 128][causal];
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(var.threads), 0, stream, a);
+  uint64_t grid = blocks;
+  if (var.persist[bf16] && d == 128 && !causal && N % fa2::kSchedRows == 0) {
+    fn = var.persist[bf16];
+    grid = std::min<uint64_t>(blocks, (uint64_t)cu_count());
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(var.threads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }
@@ -337,8 +366,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   if (variant < 0 || variant >= kNumBwdVariants) return FA2_ERR_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_ARG;
   if (!finite_bits(scale)) return FA2_ERR_ARG;
-  if (B < 0 || H < 0 || N < 0) return FA2_ERR_SHAPE;
-  if (B == 0 || H == 0 || N == 0) return kEmpty;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA2_ERR_NULL;
   if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
   if ((uint64_t)N * (uint64_t)d * 2u >= (1ull << 32)) return FA2_ERR_SHAPE;
@@ -371,7 +399,6 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d,
             int causal, float scale, hipStream_t stream, int dtype, int variant) {
   const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, variant);
-  if (st == kEmpty) return FA2_OK;
   if (st != FA2_OK) return st;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
   const int bf16 = dtype == FA2_DTYPE_BF16;
@@ -478,8 +505,7 @@ FA2_EXPORT int fa2_fwd_variant(const void* q, const void* k, const void* v, void
 FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, int B, int H, int N, int d, int causal,
                              float scale, int dtype, int variant) {
-  const int st = check(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, variant);
-  return st == kEmpty ? FA2_OK : st;
+  return check(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, variant);
 }
 
 FA2_EXPORT int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -523,8 +549,7 @@ FA2_EXPORT int fa2_bwd_check(const void* q, const void* k, const void* v, const 
                              const float* lse, const void* dout, const void* dq, const void* dk,
                              const void* dv, const float* delta, int B, int H, int N, int d,
                              int causal, float scale, int dtype) {
-  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, 0);
-  return st == kEmpty ? FA2_OK : st;
+  return check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, 0);
 }
 
 FA2_EXPORT int fa2_default_variant(int dtype, int d, int causal) {

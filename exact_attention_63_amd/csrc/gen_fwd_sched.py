@@ -81,6 +81,7 @@ R_VA = 168              # v[168:175] V^T fragment LDS addresses (d block, low/hi
 R_DSRC = 176            # v[176:177] global byte offsets of this lane's two copy chunks
 R_M, R_L, R_ALPHA = 178, 179, 180
 R_RS0, R_RS1, R_T0, R_T1 = 181, 182, 183, 184
+R_QOFF = 185            # this lane's byte offset inside a Q block: (lane % 32) * 256 + 16 (lane / 32)
 R_KBUF = 186            # K operand buffers
 R_VBUF = R_KBUF + 4 * NKB
 R_END = R_VBUF + 4 * NVB   # first VGPR the loop does not touch
@@ -95,8 +96,16 @@ S_M0B = 52              # LDS address of this wave's 2 KiB share of a tile
 S_TM1 = 53              # T - 1
 S_J2 = 54               # j + 2
 S_J3 = 55               # j + 3
-S_RET = 56              # s[56:57]: return address of the exact-update path
-SGPR_CLOBBER = [S_J, S_SOFF, S_TM1, S_J2, S_J3, S_RET, S_RET + 1]
+S_RET = 54              # s[54:55]: return address of the exact-update path (j + 2, j + 3
+                        # are not needed after it: end_interval recomputes j + 3)
+# The next work item of a persistent workgroup (when s{S_HASN} != 0): its K and
+# V descriptors (they replace the current ones once the current item's copies
+# are done), its Q descriptor and the byte offset of its query block.
+S_NKD, S_NVD, S_NQD = 56, 60, 64
+S_NQOFF = 68
+S_HASN = 69
+S_TMP = 70
+SGPR_CLOBBER = [S_J, S_SOFF, S_TM1, S_J2, S_J3, S_TMP]
 
 
 def vr(lo, n=1):
@@ -250,20 +259,53 @@ def dma_parts(a, k, name):
     (k+3) % 4 (last read by the scores of tile j-1 in interval j-2, or by
     the exact update of tile j-1 in interval j-1) and V of tile j+2 into V
     stage (k+2) % 4 (last read by P.V(j-2) in interval j-1), as four
-    one-instruction pieces (this wave's two 1 KiB blocks of each), each
-    guarded by its tile-exists test.  K(j+3) is first read in interval j+2,
-    V(j+2) at the end of interval j+2.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
+    one-instruction pieces (this wave's two 1 KiB blocks of each).  K(j+3) is
+    first read in interval j+2, V(j+2) at the end of interval j+2.  Past the
+    item's last tile, the same slots copy the next item's K tiles 0-2 and V
+    tiles 0-1 (its tile t follows tile T - 1 in the ring, T % 4 == 0), so
+    that its loop finds them in stages 0-2.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
     parts = []
-    for which, (jr, desc, base) in enumerate(((S_J3, S_KDESC, ((k + 3) % 4) * TSZ),
-                                              (S_J2, S_VDESC, VOFF + ((k + 2) % 4) * TSZ))):
+    for which, (jr, desc, base, nnext) in enumerate(((S_J3, S_KDESC, ((k + 3) % 4) * TSZ, 3),
+                                                     (S_J2, S_VDESC, VOFF + ((k + 2) % 4) * TSZ, 2))):
         for kk in range(2):
-            lbl = a.lbl(f"{name}c{which}{kk}")
-            parts.append([f"s_cmp_lt_u32 s{jr}, s{S_T}", f"s_cbranch_scc0 {lbl}",
-                          f"s_lshl_b32 s{S_SOFF}, s{jr}, 14",
-                          f"s_add_u32 m0, s{S_M0B}, {base + 1024 * kk}", "s_nop 0",
+            cur = a.lbl(f"{name}c{which}{kk}c")
+            go = a.lbl(f"{name}c{which}{kk}g")
+            skip = a.lbl(f"{name}c{which}{kk}s")
+            parts.append([f"s_cmp_lt_u32 s{jr}, s{S_T}", f"s_cbranch_scc1 {cur}",
+                          f"s_cmp_eq_u32 s{S_HASN}, 0", f"s_cbranch_scc1 {skip}",
+                          f"s_sub_u32 s{S_TMP}, s{jr}, s{S_T}",
+                          f"s_cmp_lt_u32 s{S_TMP}, {nnext}", f"s_cbranch_scc0 {skip}",
+                          f"s_lshl_b32 s{S_SOFF}, s{S_TMP}, 14", f"s_branch {go}",
+                          f"{cur}:", f"s_lshl_b32 s{S_SOFF}, s{jr}, 14",
+                          f"{go}:", f"s_add_u32 m0, s{S_M0B}, {base + 1024 * kk}", "s_nop 0",
                           f"buffer_load_dwordx4 {vr(R_DSRC + kk)}, s[{desc}:{desc + 3}], s{S_SOFF} offen lds",
-                          f"{lbl}:"])
+                          f"{skip}:"])
     return parts
+
+
+def switch_descriptors(a, name):
+    """Once the current item's K (V) copies are done -- from interval T - 3
+    (T - 2) on -- the K (V) descriptor becomes the next item's."""
+    for jr, cur, nxt in ((S_J3, S_KDESC, S_NKD), (S_J2, S_VDESC, S_NVD)):
+        lbl = a.lbl(f"{name}sw{cur}")
+        a(f"s_cmp_eq_u32 s{jr}, s{S_T}")
+        a(f"s_cbranch_scc0 {lbl}")
+        a(f"s_cmp_eq_u32 s{S_HASN}, 0")
+        a(f"s_cbranch_scc1 {lbl}")
+        a(f"s_mov_b64 s[{cur}:{cur + 1}], s[{nxt}:{nxt + 1}]")
+        a(f"s_mov_b64 s[{cur + 2}:{cur + 3}], s[{nxt + 2}:{nxt + 3}]")
+        a(f"{lbl}:")
+
+
+def load_next_q(a, name):
+    """The next item's Q fragments into v[0:31] (free: the last interval has
+    no score MFMA and no exact update)."""
+    lbl = a.lbl(f"{name}nq")
+    a(f"s_cmp_eq_u32 s{S_HASN}, 0")
+    a(f"s_cbranch_scc1 {lbl}")
+    for dk in range(DK):
+        a(f"buffer_load_dwordx4 {q_frag(dk)}, v{R_QOFF}, s[{S_NQD}:{S_NQD + 3}], s{S_NQOFF} offen offset:{32 * dk}")
+    a(f"{lbl}:")
 
 
 def dma_half(a, desc, base):
@@ -277,11 +319,15 @@ def dma_half(a, desc, base):
 def end_interval(a, name):
     """Interval j+1 reads K(j+2) and V(j+1) (its last instructions prefetch
     V^T operands of P.V(j+1)), both copied in interval j-1: wait for this
-    wave's copies issued before interval j -- the ones of interval j (K(j+3),
-    V(j+2)) stay in flight when both exist, else wait for every copy -- then
-    the barrier publishes them."""
+    wave's copies issued before interval j -- the four of interval j stay in
+    flight when it issued four (j + 3 < T, or a next item), else wait for
+    every copy -- then the barrier publishes them."""
+    a(f"s_add_u32 s{S_J3}, s{S_J}, 3")
     a(f"s_cmp_lt_u32 s{S_J3}, s{S_T}")
-    a(f"s_cbranch_scc0 {a.lbl(name + 'w0')}")
+    a(f"s_cbranch_scc1 {a.lbl(name + 'w4')}")
+    a(f"s_cmp_eq_u32 s{S_HASN}, 0")
+    a(f"s_cbranch_scc1 {a.lbl(name + 'w0')}")
+    a(f"{a.lbl(name + 'w4')}:")
     a("s_waitcnt vmcnt(4)")
     a(f"s_branch {a.lbl(name + 'wb')}")
     a(f"{a.lbl(name + 'w0')}:")
@@ -352,9 +398,12 @@ class Rounds:
     (at least one MFMA) after it is made.  The chunks (3 or 4 VALU
     instructions each) are spread evenly over the MFMA slots of an interval."""
 
-    def __init__(self, a, buf):
+    def __init__(self, a, buf, exact_max=False):
         self.a = a
         self.rounds = []
+        if exact_max:
+            # the last tile of an item: m_new = max(m, max S c), alpha, first
+            self.rounds += exact_reference(a, buf)
         for r in range(16 + 2):
             if 0 <= r - 2 < 16:
                 self.rounds.append(pair_sum(a, buf, r - 2))
@@ -376,6 +425,20 @@ class Rounds:
 
     def finish(self):
         self.emit_upto(1, 1)
+
+
+def exact_reference(a, buf):
+    """Chunks that set the row's reference to max(m, max S c) of the scores in
+    buffer buf and alpha = 2^(m_old - m_new)."""
+    sub = Asm(a.dt, a.tag)
+    row_max(sub, buf)
+    sub(f"v_mul_f32 v{R_T0}, s{S_C}, v{R_T0}")
+    sub(f"v_max_f32 v{R_T1}, v{R_M}, v{R_T0}")
+    sub(f"v_sub_f32 v{R_T0}, v{R_M}, v{R_T1}")
+    sub(f"v_mov_b32 v{R_M}, v{R_T1}")
+    sub(f"v_exp_f32 v{R_ALPHA}, v{R_T0}")
+    lines = sub.lines
+    return [lines[i:i + 4] for i in range(0, len(lines), 4)]
 
 
 def pair_regs(buf, q):
@@ -422,6 +485,7 @@ def body(a, k, last, first):
     rd = Reads(a) if first else seeded_reads(a)
     a(f"s_add_u32 s{S_J2}, s{S_J}, 2")
     a(f"s_add_u32 s{S_J3}, s{S_J}, 3")
+    switch_descriptors(a, name)
     # the copies go out one at a time, after MFMAs 2, 6, 10 and 14 of the
     # interval (all at once when it has no MFMA): issued back to back right
     # after the barrier by every wave, they measured 1-2 % slower
@@ -429,7 +493,7 @@ def body(a, k, last, first):
     if not first:
         rescale(a, name + "r")       # alpha still holds tile j-1's factor
     softmax_start(a)
-    rounds = Rounds(a, cur)
+    rounds = Rounds(a, cur, exact_max=last)
     nslots = (0 if first else 16) + (0 if last else 16)
     slot = [0]
 
@@ -441,6 +505,9 @@ def body(a, k, last, first):
         for n in copy_at.get(slot[0], []):
             for ins in parts[n]:
                 a(ins)
+        if last and slot[0] == 1:
+            # Q's last reader was the final score MFMA of the interval before
+            load_next_q(a, name)
         slot[0] += 1
         rounds.emit_upto(slot[0], nslots)
 
@@ -458,8 +525,15 @@ def body(a, k, last, first):
         for part in parts:
             for ins in part:
                 a(ins)
+        if last:
+            load_next_q(a, name)
     rounds.finish()
-    softmax_check(a, k)
+    if last:
+        # reference from the exact row max: p <= 1, no check, no exact update
+        a(f"v_add_f32 v{R_T0}, v{R_RS0}, v{R_RS1}")
+        a(f"v_fma_f32 v{R_L}, v{R_L}, v{R_ALPHA}, v{R_T0}")
+    else:
+        softmax_check(a, k)
     # P.V(j) opens the next interval (or follows the last one)
     v_prefetch(Reads(a, vstart=V_START_LAST if last else 0), k)
     end_interval(a, name)
@@ -488,12 +562,9 @@ def exact_update(a, k):
     score_phase(a, Reads(a), k, buf, False, look=LK_EXACT)
     a("s_nop 7")
     a("s_nop 4")     # MFMA result -> VALU read
-    row_max(a, buf)
-    a(f"v_mul_f32 v{R_T0}, s{S_C}, v{R_T0}")
-    a(f"v_max_f32 v{R_T1}, v{R_M}, v{R_T0}")
-    a(f"v_sub_f32 v{R_RS1}, v{R_M}, v{R_T1}")
-    a(f"v_exp_f32 v{R_ALPHA}, v{R_RS1}")
-    a(f"v_mov_b32 v{R_M}, v{R_T1}")
+    for chunk in exact_reference(a, buf):
+        for ins in chunk:
+            a(ins)
     a(f"v_mov_b32 v{R_RS0}, 0")
     a(f"v_mov_b32 v{R_RS1}, 0")
     for q in range(16):
@@ -505,12 +576,13 @@ def exact_update(a, k):
 
 
 def prologue(a):
-    """K of tiles 0-2 and V of tiles 0-1 were copied before the block: wait
-    for this wave's copies, publish them, S(0) into buffer 0, m = exact row
-    max of tile 0."""
+    """K of tiles 0-2 and V of tiles 0-1 are in stages 0-2 (copied by the C++
+    side, which waited for them, or by the previous item's last intervals,
+    waited for at the end of its block): publish them, S(0) into buffer 0,
+    m = exact row max of tile 0.  (No vmcnt wait here: the stores of the
+    previous item's output may still be in flight.)"""
     a(f"s_mov_b32 s{S_J}, 0")
     a(f"s_add_u32 s{S_TM1}, s{S_T}, -1")
-    a("s_waitcnt vmcnt(0)")
     a("s_barrier")
     score_phase(a, Reads(a, kstart=K_START_PROLOGUE), 0, 0, False)
     a(f"v_mov_b32 v{R_L}, 0")
@@ -537,14 +609,15 @@ def block(dtype):
     for k in range(4):
         exact_update(a, k)
     a(f"{a.lbl('done')}:")
-    a("s_waitcnt vmcnt(0) lgkmcnt(0)")
+    a("s_waitcnt vmcnt(0) lgkmcnt(0)")   # the next item's Q and copies have landed
     a("s_nop 7")
     a("s_nop 7")     # MFMA results -> the C++ code that reads acc
     return a.lines
 
 
 def clobbers():
-    regs = [f'"v{r}"' for r in range(R_S, R_S + 64)] + [f'"v{r}"' for r in range(R_M + 2, R_END)]
+    regs = [f'"v{r}"' for r in range(R_S, R_S + 64)]
+    regs += [f'"v{r}"' for r in range(R_M + 2, R_END) if r != R_QOFF]
     regs += [f'"s{s}"' for s in SGPR_CLOBBER]
     return ", ".join(regs + ['"m0"', '"vcc"', '"scc"', '"memory"'])
 

@@ -38,9 +38,9 @@
  * Errors.  Arguments are validated on the host before any HIP call; when a
  * check fails nothing is launched, o and lse are left untouched and a negative
  * status is returned.  Checks run in this order, the first failure wins:
- * dtype / causal / scale / variant (FA2_ERR_ARG), negative sizes
- * (FA2_ERR_SHAPE), empty problem (B, H or N == 0: FA2_OK, nothing is read or
- * written and the pointers are not inspected), NULL pointers (FA2_ERR_NULL),
+ * dtype / causal / scale / variant (FA2_ERR_ARG), B, H or N below 1
+ * (FA2_ERR_SHAPE: an empty problem is the caller's no-op, the library is not
+ * called for it), NULL pointers (FA2_ERR_NULL),
  * d (FA2_ERR_UNSUPPORTED), size limits (FA2_ERR_SHAPE), alignment
  * (FA2_ERR_ALIGN), overlap (FA2_ERR_ALIAS).  Faults that happen while the
  * kernel runs surface at the caller's synchronisation, not here.
@@ -58,7 +58,7 @@ extern "C" {
 enum fa2_status {
     FA2_OK = 0,
     FA2_ERR_NULL = -1,        /* a tensor pointer is NULL                                  */
-    FA2_ERR_SHAPE = -2,       /* B, H or N < 0, or a tensor or one head is too large       */
+    FA2_ERR_SHAPE = -2,       /* B, H or N < 1, or a tensor or one head is too large       */
     FA2_ERR_UNSUPPORTED = -3, /* d is not 64 or 128                                         */
     FA2_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                    */
     FA2_ERR_ARG = -5,         /* scale not finite, causal not 0/1, bad dtype or variant     */
@@ -80,7 +80,7 @@ enum fa2_dtype {
  *                  overlap any other argument
  *   lse      [out] device, [B,H,N] float32, 16-byte aligned, must not overlap
  *                  q, k, v or o
- *   B, H, N        batch, heads, sequence length; each >= 0 (0 is a no-op).
+ *   B, H, N        batch, heads, sequence length; each >= 1.
  *                  N*d*2 bytes (one head) must stay below 2^32 and B*H*N*d
  *                  below 2^62.
  *   d              head dimension: 64 or 128

@@ -236,7 +236,12 @@ class Wave:
     def complete_vm(self, keep):
         while len(self.vm_q) > keep:
             c = self.vm_q.pop(0)
-            self.emu.lds_write(c, self)
+            if "regs" in c:
+                lo, hi = c["regs"]
+                self.v[lo:hi + 1] = c["data"]
+                self.pending[lo:hi + 1] = False
+            else:
+                self.emu.lds_write(c, self)
 
     # ---- execute one instruction ---------------------------------------------
     def step(self):
@@ -266,6 +271,14 @@ class Wave:
             return
         elif op == "s_mov_b32":
             self.sset(args[0], self.ssrc(args[1]))
+        elif op == "s_mov_b64":
+            dlo, _ = srange(args[0])
+            slo, _ = srange(args[1])
+            self.s[dlo], self.s[dlo + 1] = self.s[slo], self.s[slo + 1]
+        elif op == "s_sub_u32":
+            r = self.ssrc(args[1]) - self.ssrc(args[2])
+            self.scc = r < 0
+            self.sset(args[0], r & 0xFFFFFFFF)
         elif op == "s_add_u32":
             r = self.ssrc(args[1]) + self.ssrc(args[2])
             self.scc = r > 0xFFFFFFFF
@@ -302,8 +315,10 @@ class Wave:
             nxt = prog.addr_to_index[a]
         elif op == "ds_read_b128" or op == "ds_read_b64_tr_b16":
             self.ds_read(op, args)
-        elif op == "buffer_load_dwordx4":
+        elif op == "buffer_load_dwordx4" and "lds" in line:
             self.lds_copy(args, line)
+        elif op == "buffer_load_dwordx4":
+            self.vgpr_load(args, line)
         elif op.startswith("v_mfma_f32_32x32x16_"):
             self.mfma(op, args)
         elif op.startswith("v_"):
@@ -463,6 +478,29 @@ class Wave:
             data = out.view(np.uint32).T.copy()            # (2, 64)
         self.pending[dlo:dhi + 1] = True
         self.lds_q.append(((dlo, dhi), data))
+
+    def vgpr_load(self, args, line):
+        """buffer_load_dwordx4 vD, vOff, s[desc], sOff offen offset:N: lane l
+        reads 16 bytes at sOff + vOff[l] + N (zeros past the buffer)."""
+        dlo, dhi = vrange(args[0])
+        vlo, _ = vrange(args[1])
+        blo, _ = srange(args[2])
+        toks = args[3].split()
+        soff = self.ssrc(toks[0])
+        m = re.search(r"offset:(\d+)", args[3])
+        off = int(m.group(1)) if m else 0
+        if "offen" not in toks or dhi - dlo != 3:
+            self.err("unsupported buffer load form")
+        voff = self.rd_v(vlo, vlo)[0].astype(np.int64)
+        buf = self.emu.buffers[self.s[blo]]
+        data = np.zeros((LANES, 16), dtype=np.uint8)
+        for l in range(LANES):
+            g = soff + int(voff[l]) + off
+            if g + 16 <= len(buf):
+                data[l] = np.frombuffer(buf, dtype=np.uint8, count=16, offset=g)
+        self.wr_v(dlo, dhi, "load")
+        self.pending[dlo:dhi + 1] = True
+        self.vm_q.append({"regs": (dlo, dhi), "data": data.view(np.uint32).T.copy()})
 
     def lds_copy(self, args, line):
         if "offen lds" not in line:

@@ -125,9 +125,11 @@ def test_inputs_may_alias_each_other(lib):
     assert chk(k=Q, v=Q) == fa2.FA2_OK
 
 
-def test_empty_problem_is_a_noop(lib):
-    for kw in (dict(B=0), dict(H=0), dict(N=0)):
-        assert chk(q=None, k=None, v=None, o=None, lse=None, **kw) == fa2.FA2_OK
+def test_empty_problem_is_a_shape_error(lib):
+    # B, H or N below 1 is FA2_ERR_SHAPE, checked before the pointers
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(N=-5)):
+        assert chk(**kw) == fa2.FA2_ERR_SHAPE
+        assert chk(q=None, k=None, v=None, o=None, lse=None, **kw) == fa2.FA2_ERR_SHAPE
 
 
 def test_adjacent_buffers_do_not_alias(lib):
@@ -193,10 +195,11 @@ def test_bwd_invalid_arguments(lib, kw, status):
     assert bchk(**kw) == status
 
 
-def test_bwd_empty_problem_is_a_noop(lib):
+def test_bwd_empty_problem_is_a_shape_error(lib):
     none = dict(q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None, delta=None)
-    for kw in (dict(B=0), dict(H=0), dict(N=0)):
-        assert bchk(**none, **kw) == fa2.FA2_OK
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(H=-2)):
+        assert bchk(**kw) == fa2.FA2_ERR_SHAPE
+        assert bchk(**none, **kw) == fa2.FA2_ERR_SHAPE
 
 
 def test_bwd_adjacent_outputs_do_not_alias(lib):

@@ -210,3 +210,78 @@ def test_emulator_catches_a_missing_barrier():
         del lines[i]
         return lines
     assert "copy" in _planted(mutate)
+
+
+# ---- persistent workgroups: one workgroup runs several items in a row ------
+
+def _desc(s, base, buf_id, nbytes):
+    s[base], s[base + 1], s[base + 2], s[base + 3] = buf_id, 0, nbytes, 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_consecutive_items(dtype):
+    """Three items (head, query block) of different heads through one
+    workgroup: each loop copies the next item's first K/V tiles and loads its
+    Q in its last intervals, the next loop starts from them."""
+    rng = np.random.default_rng(21)
+    N, T = 512, 8
+    heads = [tuple(rng.standard_normal((N, D), dtype=np.float32) for _ in range(3)) for _ in range(2)]
+    items = [(0, 1), (1, 0), (1, 1)]          # (head, query block)
+    scale = 1 / math.sqrt(D)
+    c = scale * math.log2(math.e)
+    bits = [tuple(bits16(x, dtype)[0] for x in h) for h in heads]
+    f64 = [tuple(bits16(x, dtype)[1] for x in h) for h in heads]
+    buffers = {}
+    for h, (qb_, kb_, vb_) in enumerate(bits):
+        buffers[10 + 3 * h], buffers[11 + 3 * h], buffers[12 + 3 * h] = qb_.tobytes(), kb_.tobytes(), vb_.tobytes()
+    dt = "bf16" if dtype == "bf16" else "f16"
+    text = "\n".join(GEN.block(dt))
+    state = None
+    for i, (h, qblk) in enumerate(items):
+        emu = Emulator([text] * 8, 128 * 1024, buffers)
+        for w, wave in enumerate(emu.waves):
+            init_wave(w, wave, bits[h][0], N, qblk, T, c)
+            if state is not None:                 # the previous block's registers and LDS
+                wave.v[:GEN.R_Q + 32] = state[0][w][:GEN.R_Q + 32]
+            lanes = np.arange(64)
+            wave.v[GEN.R_QOFF] = (lanes % 32) * 256 + 16 * (lanes // 32)
+            _desc(wave.s, GEN.S_KDESC, 11 + 3 * h, N * 256)
+            _desc(wave.s, GEN.S_VDESC, 12 + 3 * h, N * 256)
+            if i + 1 < len(items):
+                hn, qn = items[i + 1]
+                _desc(wave.s, GEN.S_NKD, 11 + 3 * hn, N * 256)
+                _desc(wave.s, GEN.S_NVD, 12 + 3 * hn, N * 256)
+                _desc(wave.s, GEN.S_NQD, 10 + 3 * hn, N * 256)
+                wave.s[GEN.S_NQOFF] = (qn * 256 + 32 * w) * 256
+                wave.s[GEN.S_HASN] = 1
+        if state is None:
+            for tile in range(3):
+                halves = [(bits[h][1], tile * GEN.TSZ)] + ([(bits[h][2], GEN.VOFF + tile * GEN.TSZ)] if tile < 2 else [])
+                for src, base in halves:
+                    for r in range(64):
+                        for p in range(16):
+                            row, ch = tile * 64 + r, p ^ swz(r)
+                            dst = base + r * 256 + 16 * p
+                            emu.lds[dst:dst + 16] = np.frombuffer(src[row, 8 * ch:8 * ch + 8].tobytes(), dtype=np.uint8)
+        else:
+            emu.lds[:] = state[1]
+        emu.run()
+        state = ([wave.v.copy() for wave in emu.waves], emu.lds.copy())
+        # this item's output
+        o = np.zeros((256, D))
+        lse = np.zeros(256)
+        for w, wave in enumerate(emu.waves):
+            accf = wave.v[GEN.R_ACC:GEN.R_ACC + 64].view(np.float32).astype(np.float64)
+            m = wave.v[GEN.R_M].view(np.float32).astype(np.float64)
+            l = wave.v[GEN.R_L].view(np.float32).astype(np.float64)
+            ltot = l[:32] + l[32:]
+            for db in range(4):
+                for r in range(16):
+                    for lh in range(2):
+                        d = 32 * db + 8 * (r // 4) + 4 * lh + r % 4
+                        o[32 * w:32 * w + 32, d] = accf[16 * db + r, 32 * lh:32 * lh + 32] / ltot
+            lse[32 * w:32 * w + 32] = (m[:32] + np.log2(ltot)) * math.log(2)
+        rows = np.arange(qblk * 256, qblk * 256 + 256)
+        o_ref, l_ref = oracle.attention_3pass(*f64[h], False, scale, rows=rows)
+        assert np.abs(o - o_ref).max() <= TOL_O[dtype], (i, np.abs(o - o_ref).max())
+        assert np.abs(lse - l_ref).max() <= 1e-3, i
