@@ -62,7 +62,7 @@ constexpr Variant make_roles_variant(const char* name) {
 // The scheduled kernel (fa2_fwd_sched.hpp) at d = 128; d = 64 runs the
 // 128-key-tile kernel of the same workgroup shape (8 waves, 256 rows).
 constexpr Variant make_sched_variant(const char* name) {
-  using D64 = Tile<8, 1, 4, 2, 5, 4>;
+  using D64 = Tile<8, 1, 4, 2, 2, 4>;
   return Variant{name,
                  512,
                  fa2::kSchedRows,
@@ -82,53 +82,36 @@ constexpr Variant make_sched_persist_variant(const char* name) {
 }
 
 // Index 0 is the tuned default; it is resolved per (dtype, d, causal) by
-// default_variant() below.
+// default_variant() below.  Besides the defaults the table keeps the plain
+// register-staged loop (the simplest form of the method), the previous d = 128
+// default (the compiler-scheduled loop the hand-scheduled one replaced), the
+// software-exp2 alternative and the role-split kernel.
 const Variant kVariants[] = {
-    {"default", 0, 0, {}},
-    make_variant<Tile<4, 1, 2, 2>>("w4_q32_k64_occ2"),   // 4 waves x 32 rows, 64-key tiles, 2 waves/SIMD
-    make_variant<Tile<4, 2, 2, 1>>("w4_q64_k64_occ1"),   // 4 waves x 64 rows, 64-key tiles, 1 wave/SIMD
-    make_variant<Tile<8, 1, 2, 2>>("w8_q32_k64_occ2"),   // 8 waves x 32 rows, 64-key tiles, 2 waves/SIMD
-    make_variant<Tile<4, 1, 2, 2, 1>>("w4_q32_k64_occ2_pipe"),    // variant 1, software-pipelined loop
-    make_variant<Tile<8, 1, 2, 2, 1>>("w8_q32_k64_occ2_pipe"),    // variant 3, software-pipelined loop
-    make_variant<Tile<4, 1, 2, 2, 2>>("w4_q32_k64_occ2_ilv"),     // variant 4 + MFMA/VALU interleave
-    make_variant<Tile<8, 1, 2, 2, 2>>("w8_q32_k64_occ2_ilv"),     // variant 5 + MFMA/VALU interleave
-    make_variant<Tile<8, 1, 2, 2, 3>>("w8_q32_k64_pingpong"),     // two 4-wave groups in opposite phases
-    make_variant<Tile<8, 1, 2, 2, 4>>("w8_q32_k64_dma3"),         // direct global->LDS copies, 3 stages
-    make_variant<Tile<4, 1, 2, 2, 5>>("w4_q32_k64_dma2"),         // 4 waves, 2 stages: two workgroups per CU
-    make_variant<Tile<8, 1, 2, 2, 4, 4>>("w8_q32_k64_dma3_look4"), // dma3 + 4 operand reads ahead
-    make_variant<Tile<8, 1, 2, 2, 4, 6>>("w8_q32_k64_dma3_look6"), // dma3 + 6 operand reads ahead
-    make_variant<Tile<8, 1, 4, 2, 5>>("w8_q32_k128_dma2"),        // 128-key tiles, 2-stage ring
-    make_variant<Tile<8, 1, 4, 2, 5, 4>>("w8_q32_k128_dma2_look4"), // ... with 4 operand reads ahead
-    make_variant<Tile<8, 1, 2, 2, 4, 0, 4>>("w8_q32_k64_dma3_pre4"),   // dma3 + 4 P.V operands read before the softmax
-    make_variant<Tile<8, 1, 2, 2, 7, 0, 0>>("w8_q32_k64_dma4_pairs"),  // 4-stage ring, one barrier per 2 tiles
-    make_variant<Tile<8, 1, 2, 2, 4, 0, 0, true>>("w8_q32_k64_dma3_asmcp"),   // dma3, copies as assembly
-    make_variant<Tile<8, 1, 2, 2, 9, 4>>("w8_q32_k64_dma4_pingpong_look4"),   // two wave groups in opposite phases
-    make_variant<Tile<8, 1, 2, 2, 4, 0, 0, false, 4>>("w8_q32_k64_dma3_asm4"),   // dma3, MFMA phases as assembly, 4 ahead
-    make_variant<Tile<8, 1, 2, 2, 9, 0, 0, false, 8>>("w8_q32_k64_dma4_pingpong_asm8"),  // ... MFMA phases as assembly, 8 ahead
-    make_variant<Tile<4, 1, 2, 2, 5, 4>>("w4_q32_k64_dma2_look4"),   // 4 waves, 2 workgroups per CU, 4 operand reads ahead
-    make_variant<Tile<8, 1, 2, 2, 10, 0, 4>>("w8_q32_k32_dma4_thread4"),   // softmax threaded between MFMAs, 4 operands ahead
-    make_variant<Tile<8, 1, 2, 2, 11, 4>>("w8_q32_k64_dma3_shift_look4"),  // waves 0-3 one phase ahead of waves 4-7
-    make_roles_variant("w8_pairs32_k64_roles_ring3"),  // softmax wave + P.V wave per SIMD, P through LDS
-    make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 1>>("w8_q32_k64_dma3_look4_swexp"),      // variant 11, every 2^x in software
-    make_variant<Tile<8, 1, 2, 2, 4, 4, 0, false, 0, 2>>("w8_q32_k64_dma3_look4_swexp_half"), // variant 11, every other 2^x in software
-    make_sched_variant("w8_q32_k64_sched_ring4"),   // hand-scheduled main loop, waves paired half a tile apart
-    make_sched_persist_variant("w8_q32_k64_sched_persist"),   // ... one workgroup per CU over the items
+    {"default", 0, 0, {}, {nullptr, nullptr}},
+    make_variant<Tile<4, 1, 2, 2>>("w4_q32_k64_occ2"),                // 1: register-staged 2-stage ring, 4 waves x 32 rows
+    make_variant<Tile<4, 1, 2, 2, 2>>("w4_q32_k64_dma2"),             // 2: direct copies, 2 stages, two workgroups per CU
+    make_variant<Tile<8, 1, 4, 2, 2, 4>>("w8_q32_k128_dma2_look4"),   // 3: 128-key tiles, 2 stages, 4 operand reads ahead
+    make_variant<Tile<8, 1, 2, 2, 3, 4>>("w8_q32_k64_dma3_look4"),    // 4: 64-key tiles, 3 stages, 4 operand reads ahead
+    make_variant<Tile<8, 1, 2, 2, 3, 4, 2>>("w8_q32_k64_dma3_look4_swexp_half"),  // 5: variant 4, every other 2^x in software
+    make_roles_variant("w8_pairs32_k64_roles_ring3"),                 // 6: softmax wave + P.V wave per SIMD, P through LDS
+    make_sched_variant("w8_q32_k64_sched_ring4"),                     // 7: hand-scheduled d = 128 loop
+    make_sched_persist_variant("w8_q32_k64_sched_persist"),           // 8: ... persistent where the shape allows
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-static_assert(kNumVariants == 29, "variant table");
+static_assert(kNumVariants == 9, "variant table");
 
-// Measured on MI355X (same box, alternating runs): d = 128, causal or not,
-// runs the hand-scheduled kernel (variant 27: headline shape 0.49-0.50 ms
-// per call against 0.52-0.53 for variant 11, N = 16384 causal 1.84 against
-// 1.88 ms, N = 4096 causal a tie); non-causal d = 64 runs 128-key tiles in a
-// 2-stage ring with 4 operand reads ahead (variant 14); causal d = 64 runs
-// 4-wave workgroups, two per CU, on a 2-stage ring of 64-key tiles (variant
-// 10: twice the workgroups balance the triangular work).
-constexpr int kSchedVariant = 27;
+// Measured on MI355X (same box, alternating runs): d = 128 runs the
+// hand-scheduled loop, persistent for non-causal N % 256 == 0 (headline shape
+// 0.471 ms against 0.483 for one workgroup per item and 0.52-0.53 for variant
+// 4; N = 16384 causal 1.84 against 1.88 ms); non-causal d = 64 runs 128-key
+// tiles in a 2-stage ring with 4 operand reads ahead (variant 3); causal
+// d = 64 runs 4-wave workgroups, two per CU, on a 2-stage ring of 64-key
+// tiles (variant 2: twice the workgroups balance the triangular work).
+constexpr int kSchedVariant = 8;
 int default_variant(int bf16, int d, int causal) {
   (void)bf16;
   if (d == 128) return kSchedVariant;
-  return causal ? 10 : 14;
+  return causal ? 2 : 3;
 }
 
 // compute units of the current device (one persistent workgroup each)
@@ -238,28 +221,16 @@ using QTile = BwdTile<8, 2>;
 // dQ alternative for small grids: 4 waves (128 queries) per workgroup
 using QTile4 = BwdTile<4, 2>;
 
-// dK/dV alternative: 8 waves (128 keys), two per SIMD, the dV and dK
-// products split between the two waves of a SIMD.
-constexpr int kSplitKeys = 128;
+// dK/dV with P handed between the two waves of a SIMD: 8 waves (128 keys).
+constexpr int kPairKeys = 128;
 
 struct BwdKernels {
   delta_fn delta[2][2];        // [bf16][d == 128]
   bwd_fn dkdv[2][2][2];        // [bf16][d == 128][causal]
-  bwd_fn dkdv_split[2][2][2];
-  bwd_fn dkdv_ring[2][2][2];
-  bwd_fn dkdv_ring_sub2[2][2][2];
-  bwd_fn dkdv_pair[2][2][2];
-  bwd_fn dkdv_pair_look[2][2][2];
-  bwd_fn dkdv_pair_look2[2][2][2];
-  bwd_fn dkdv_pair_look6[2][2][2];
-  bwd_fn dkdv_pipe[2][2][2];
+  bwd_fn dkdv_pair[2][2][2];   // P hand-off, 4 operand reads ahead
+  bwd_fn dkdv_pipe[2][2][2];   // P hand-off pipelined across query tiles, 2 reads ahead
   bwd_fn dq[2][2][2];
-  bwd_fn dq_ring[2][2][2];
-  bwd_fn dq_look[2][2][2];
-  bwd_fn dq_look2[2][2][2];
-  bwd_fn dq_look6[2][2][2];
-  bwd_fn dq_look_fused[2][2][2];
-  bwd_fn dq_pipe[2][2][2];
+  bwd_fn dq_look[2][2][2];     // 4 operand reads ahead
   bwd_fn dq4_look[2][2];       // [bf16][causal], d = 64 only
 };
 
@@ -268,44 +239,22 @@ constexpr void fill_bwd(BwdKernels& t) {
   t.delta[BF16][D == 128] = fa2::fa2_bwd_delta_kernel<BF16, D>;
   t.dkdv[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_kernel<BF16, D, false, KvTile>;
   t.dkdv[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_kernel<BF16, D, true, KvTile>;
-  t.dkdv_split[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, false>;
-  t.dkdv_split[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, false>;
-  t.dkdv_ring[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true>;
-  t.dkdv_ring[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true>;
-  t.dkdv_ring_sub2[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, false, true, 2>;
-  t.dkdv_ring_sub2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_split_kernel<BF16, D, true, true, 2>;
-  t.dkdv_pair[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false>;
-  t.dkdv_pair[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true>;
-  t.dkdv_pair_look[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 4>;
-  t.dkdv_pair_look[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 4>;
-  t.dkdv_pair_look2[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 2>;
-  t.dkdv_pair_look2[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 2>;
-  t.dkdv_pair_look6[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 6>;
-  t.dkdv_pair_look6[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 6>;
+  t.dkdv_pair[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, false, 4>;
+  t.dkdv_pair[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pair_kernel<BF16, D, true, 4>;
   t.dkdv_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, false, 2>;
   t.dkdv_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dkdv_pipe_kernel<BF16, D, true, 2>;
   t.dq[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile>;
   t.dq[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile>;
-  t.dq_ring[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, true>;
-  t.dq_ring[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, true>;
-  t.dq_look[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4>;
-  t.dq_look[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4>;
-  t.dq_look2[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 2>;
-  t.dq_look2[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 2>;
-  t.dq_look6[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 6>;
-  t.dq_look6[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 6>;
-  t.dq_look_fused[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, false, 4, true>;
-  t.dq_look_fused[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, false, 4, true>;
-  t.dq_pipe[BF16][D == 128][0] = fa2::fa2_bwd_dq_pipe_kernel<BF16, D, false, 4>;
-  t.dq_pipe[BF16][D == 128][1] = fa2::fa2_bwd_dq_pipe_kernel<BF16, D, true, 4>;
+  t.dq_look[BF16][D == 128][0] = fa2::fa2_bwd_dq_kernel<BF16, D, false, QTile, 4>;
+  t.dq_look[BF16][D == 128][1] = fa2::fa2_bwd_dq_kernel<BF16, D, true, QTile, 4>;
 }
 
 BwdKernels make_bwd_kernels() {
   BwdKernels t{};
-  t.dq4_look[0][0] = fa2::fa2_bwd_dq_kernel<false, 64, false, QTile4, false, 4>;
-  t.dq4_look[0][1] = fa2::fa2_bwd_dq_kernel<false, 64, true, QTile4, false, 4>;
-  t.dq4_look[1][0] = fa2::fa2_bwd_dq_kernel<true, 64, false, QTile4, false, 4>;
-  t.dq4_look[1][1] = fa2::fa2_bwd_dq_kernel<true, 64, true, QTile4, false, 4>;
+  t.dq4_look[0][0] = fa2::fa2_bwd_dq_kernel<false, 64, false, QTile4, 4>;
+  t.dq4_look[0][1] = fa2::fa2_bwd_dq_kernel<false, 64, true, QTile4, 4>;
+  t.dq4_look[1][0] = fa2::fa2_bwd_dq_kernel<true, 64, false, QTile4, 4>;
+  t.dq4_look[1][1] = fa2::fa2_bwd_dq_kernel<true, 64, true, QTile4, 4>;
   fill_bwd<false, 64>(t);
   fill_bwd<false, 128>(t);
   fill_bwd<true, 64>(t);
@@ -315,48 +264,29 @@ BwdKernels make_bwd_kernels() {
 
 const BwdKernels kBwd = make_bwd_kernels();
 
-// backward variants: 0 = default, 1 = one-wave-per-SIMD dK/dV kernel,
-// 2 = role-split dK/dV kernel, 3 = role-split with a 4-stage direct-copy
-// ring; 4 and 5 = variants 3 and 1 with the dQ kernel on a 3-stage
-// direct-copy ring (1-3 use the register-staged dQ kernel); 6 = variant 3
-// with 64-query tiles (two 32-query sub-blocks per barrier); 7 = P handed
-// from the dV wave to the dK wave of a SIMD through LDS (no S recomputed);
-// 8 = variant 7 with the dQ kernel's MFMAs issued with 4 operand reads ahead;
-// 9 = variant 8 with the dK/dV kernel's MFMAs ordered the same way;
-// 10 = variant 9 with D computed by the dQ kernel, which runs first (two
-// launches instead of three); 11 = variant 1 with 4-wave (128-query) dQ
-// workgroups, MFMAs 4 operand reads ahead (at d = 128 it runs variant 1's
-// dQ kernel); 12, 13 = variant 9 with 2 and 6 operand reads ahead; 14 =
-// the P hand-off pipelined across query tiles (one barrier per iteration)
-constexpr int kNumBwdVariants = 16;
-const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1", "dkdv_w8_split_occ2",
-                                                       "dkdv_w8_split_occ2_ring4",
-                                                       "dkdv_w8_split_occ2_ring4_dq_ring3",
-                                                       "dkdv_w4_occ1_dq_ring3",
-                                                       "dkdv_w8_split_occ2_ring4_q64",
-                                                       "dkdv_w8_pair_occ2_ring3_q64",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_dq_look4",
+// backward variants: 0 = default; 1 = one-wave-per-SIMD dK/dV kernel with the
+// 8-wave dQ kernel; 2 = P handed from the dV wave to the dK wave of a SIMD
+// through LDS (no S recomputed), both kernels' MFMAs issued with 4 operand
+// reads ahead; 3 = variant 1 with 4-wave (128-query) dQ workgroups, 4 reads
+// ahead (at d = 128 it runs variant 1's dQ kernel); 4 = the P hand-off
+// pipelined across query tiles (one barrier per iteration)
+constexpr int kNumBwdVariants = 5;
+const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1",
                                                        "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d",
                                                        "dkdv_w4_occ1_dq_w4_look4",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look2_dq_look2",
-                                                       "dkdv_w8_pair_occ2_ring3_q64_look6_dq_look6",
-                                                       "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4",
-                                                       "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_pipe_look4"};
+                                                       "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4"};
 
 // Measured on MI355X (bench.py --backward, alternating runs on one box): at
 // d = 128 the P hand-off between the two waves of a SIMD pipelined across
 // query tiles is fastest (headline shape 2.23-2.24 ms per call against
-// 2.35-2.40 for the unpipelined hand-off with the same operand order,
-// N = 16384 causal 8.5-8.6 against 9.4 ms; earlier steps: 2.41-2.42 without
-// the operand order, 2.42-2.45 for the role split with 64-query tiles, 2.71
-// with 32-query tiles and 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
-// against 0.130-0.133 for variants 6, 7 and 11), and for causal d = 64
-// variant 11, whose 4-wave dQ workgroups balance the triangular work
-// (0.095 against 0.103 ms).
+// 2.35-2.40 for the unpipelined hand-off, variant 2; N = 16384 causal 8.5-8.6
+// against 9.4 ms; 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
+// against 0.130-0.133 for variants 2 and 3), and for causal d = 64 variant 3,
+// whose 4-wave dQ workgroups balance the triangular work (0.095 against
+// 0.103 ms).
 int default_bwd_variant(int d, int causal) {
-  if (d == 128) return 14;
-  return causal ? 11 : 1;
+  if (d == 128) return 4;
+  return causal ? 3 : 1;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
@@ -421,49 +351,18 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   a.scale = scale;
 
   const int vi = variant == 0 ? default_bwd_variant(d, causal) : variant;
-  const bool fused_d = vi == 10;
-  auto launch_dq = [&]() {
-    if (vi == 11 && !big) {
-      a.nblk = (N + QTile4::BR - 1) / QTile4::BR;
-      hipLaunchKernelGGL(kBwd.dq4_look[bf16][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
-                         dim3(QTile4::THREADS), 0, stream, a);
-      return hipGetLastError() == hipSuccess;
-    }
-    a.nblk = (N + QTile::BR - 1) / QTile::BR;
-    bwd_fn dqfn = (vi == 4 || vi == 5) ? kBwd.dq_ring[bf16][big][causal]
-                 : (vi == 8 || vi == 9 || vi == 14) ? kBwd.dq_look[bf16][big][causal]
-                 : vi == 10             ? kBwd.dq_look_fused[bf16][big][causal]
-                 : vi == 12             ? kBwd.dq_look2[bf16][big][causal]
-                 : vi == 13             ? kBwd.dq_look6[bf16][big][causal]
-                 : vi == 15             ? kBwd.dq_pipe[bf16][big][causal]
-                                        : kBwd.dq[bf16][big][causal];
-    hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
-    return hipGetLastError() == hipSuccess;
-  };
 
-  if (fused_d) {
-    // dQ first: it computes D, uses it and writes it for the dK/dV kernel
-    if (!launch_dq()) return FA2_ERR_LAUNCH;
-  } else {
-    // D = rowsum(dO * O): one lane per 8 elements
-    const long long rows = (long long)(bh * (uint64_t)N);
-    const uint64_t lanes = (uint64_t)rows * (uint64_t)(d / 8);
-    a.nblk = 0;
-    hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
-    if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
-  }
+  // D = rowsum(dO * O): one lane per 8 elements
+  const long long rows = (long long)(bh * (uint64_t)N);
+  const uint64_t lanes = (uint64_t)rows * (uint64_t)(d / 8);
+  a.nblk = 0;
+  hipLaunchKernelGGL(kBwd.delta[bf16][big], dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, a, rows);
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
-  if (vi == 2 || vi == 3 || vi == 4 || vi == 6 || vi == 7 || vi == 8 || vi == 9 || vi == 10 || vi == 12 ||
-      vi == 13 || vi == 14 || vi == 15) {
-    a.nblk = (N + kSplitKeys - 1) / kSplitKeys;
-    bwd_fn fn = vi == 2 ? kBwd.dkdv_split[bf16][big][causal]
-              : vi == 6 ? kBwd.dkdv_ring_sub2[bf16][big][causal]
-              : (vi == 7 || vi == 8) ? kBwd.dkdv_pair[bf16][big][causal]
-              : (vi == 9 || vi == 10) ? kBwd.dkdv_pair_look[bf16][big][causal]
-              : vi == 12 ? kBwd.dkdv_pair_look2[bf16][big][causal]
-              : vi == 13 ? kBwd.dkdv_pair_look6[bf16][big][causal]
-              : (vi == 14 || vi == 15) ? kBwd.dkdv_pipe[bf16][big][causal]
-                        : kBwd.dkdv_ring[bf16][big][causal];
+  // dK, dV
+  if (vi == 2 || vi == 4) {
+    a.nblk = (N + kPairKeys - 1) / kPairKeys;
+    bwd_fn fn = vi == 2 ? kBwd.dkdv_pair[bf16][big][causal] : kBwd.dkdv_pipe[bf16][big][causal];
     hipLaunchKernelGGL(fn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(512), 0, stream, a);
   } else {
     a.nblk = (N + KvTile::BR - 1) / KvTile::BR;
@@ -472,7 +371,17 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   }
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
 
-  if (!fused_d && !launch_dq()) return FA2_ERR_LAUNCH;
+  // dQ
+  if (vi == 3 && !big) {
+    a.nblk = (N + QTile4::BR - 1) / QTile4::BR;
+    hipLaunchKernelGGL(kBwd.dq4_look[bf16][causal], dim3((unsigned)((uint64_t)a.nblk * bh)),
+                       dim3(QTile4::THREADS), 0, stream, a);
+  } else {
+    a.nblk = (N + QTile::BR - 1) / QTile::BR;
+    bwd_fn dqfn = (vi == 2 || vi == 4) ? kBwd.dq_look[bf16][big][causal] : kBwd.dq[bf16][big][causal];
+    hipLaunchKernelGGL(dqfn, dim3((unsigned)((uint64_t)a.nblk * bh)), dim3(QTile::THREADS), 0, stream, a);
+  }
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }
 

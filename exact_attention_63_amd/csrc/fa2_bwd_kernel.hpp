@@ -12,8 +12,7 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_t dO_it O_it,
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three kernels, all enqueued on the caller's stream (two when the dQ kernel
-// computes D itself, FUSED_D):
+// Three kernels, all enqueued on the caller's stream:
 //   * fa2_bwd_delta_kernel: D_i = dO_i . O_i (fp32), one row per 8 or 16
 //     lanes, written to the caller's delta buffer;
 //   * dK/dV: one workgroup per (key block, head); 32 keys per wave or per
@@ -21,15 +20,14 @@
 //     place of queries); K, V rows in VGPRs, dK^T, dV^T accumulators in
 //     registers; the query tiles (Q, dO, LSE and D) walk through LDS.  Three
 //     configurations: fa2_bwd_dkdv_kernel (each wave accumulates both, one
-//     wave per SIMD), fa2_bwd_dkdv_split_kernel (the two waves of a SIMD
-//     accumulate dV and dK of the same keys, both computing S) and
-//     fa2_bwd_dkdv_pair_kernel (the dV wave hands P to the dK wave through
-//     LDS, so every product is computed once);
+//     wave per SIMD), fa2_bwd_dkdv_pair_kernel (the dV wave hands P to the
+//     dK wave through LDS, so every product is computed once) and
+//     fa2_bwd_dkdv_pipe_kernel (the same hand-off pipelined across query
+//     tiles);
 //   * fa2_bwd_dq_kernel: one workgroup per (query block, head); each wave
 //     owns 32 queries, keeps their Q and dO rows in VGPRs and the dQ^T
 //     accumulator in registers, and walks the key tiles (K, V in LDS);
-//     options: a copy ring (RING), a fixed MFMA issue order (LOOK), D
-//     computed in the kernel (FUSED_D).
+//     option: a fixed MFMA issue order (LOOK).
 // dQ is thus produced by its own partition of the work, not by atomic adds
 // across key blocks: the result is deterministic and needs no workspace, at
 // the cost of recomputing S and dP in the dQ kernel.
@@ -402,292 +400,6 @@ void fa2_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV with the two products split between the two waves of a SIMD: one
-// workgroup per (key block of 128 keys, head), 8 waves, two per SIMD.  Wave w
-// owns keys [k_wg + 32*(w%4), +32); waves 0-3 accumulate dV^T = dO^T P and
-// waves 4-7 dK^T = Q^T dS for the same keys, so each wave holds one
-// accumulator (and the dV waves no V rows) and two waves fit in a SIMD's
-// registers.  Both recompute S = Q K_w^T (the price of the split: 10 instead
-// of 8 N^2 d MFMA FLOPs per head); only the dK waves compute dP.  Query tiles
-// of 32 rows (Q, dO, LSE in base 2, D) are staged in LDS, two stages.
-//
-// RING = false: register-staged copies, one tile ahead, two LDS stages.
-// RING = true: Q, dO, LSE and D go straight from HBM into a 4-stage LDS ring
-// (buffer_load ... lds issued as inline assembly, no staging registers),
-// three tiles ahead; each wave waits for its own copies of a tile, then one
-// barrier per tile publishes it and frees the stage of the previous tile.
-// The compiler does not see the copies (with the builtin it cannot tell the
-// ring's stages apart and drains every copy in flight before each barrier).  LSE then stays in base e in LDS
-// and is scaled by log2(e) when read.
-//
-// SUB: 32-query sub-blocks per tile (SUB = 2 needs RING): the sub-blocks of a
-// tile are processed one after the other with the same registers, so a tile
-// carries SUB times the MFMA work per barrier.
-template <bool BF16, int D, bool CAUSAL, bool RING, int SUB = 1>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void fa2_bwd_dkdv_split_kernel(BwdArgs a) {
-  using E = Elem<BF16>;
-  constexpr int T = 512, BK = 128;
-  static_assert(SUB == 1 || (SUB == 2 && RING), "two sub-blocks per tile need the copy ring");
-  constexpr int BQ = 32 * SUB;              // queries per tile
-  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
-  constexpr int TSZ = BQ * KROW;            // bytes of one Q (or dO) tile
-  // ring stages hold 64 LSE and 64 D slots (a 4-byte copy instruction fills 64)
-  constexpr int STAGE = 2 * TSZ + (RING ? 2 * 64 * 4 : 2 * BQ * 4);
-  constexpr int NS = RING ? 4 : 2;
-  constexpr int CH = BQ * D / 8;            // 16-byte chunks per tile (register staging: 512 or 256)
-  static_assert(RING || CH <= T, "one chunk per thread and tensor");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int grp = wave & 3;                 // key group
-  // waves 4-7: dK; waves 0-3: dV (read from lane 0: the role is wave-uniform)
-  const bool dk_role = __builtin_amdgcn_readfirstlane(wave) >= 4;
-
-  int bh, kblk;
-  {
-    const int i = blockIdx.x;
-    const int total = a.nblk * a.BH;
-    if constexpr (!CAUSAL) {
-      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
-      bh = logical / a.nblk;
-      kblk = logical % a.nblk;
-    } else {
-      bh = i % a.BH;
-      kblk = i / a.BH;
-    }
-  }
-  const int N = a.N;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  auto rsrc = [&](const void* p) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
-  };
-  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
-  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-
-  const int k_wg = kblk * BK;
-  const int k_w = k_wg + 32 * grp;
-  const int key = k_w + lr;
-
-  // K rows (both roles) and V rows (dK role) of the group's keys: B operands
-  u32x4 kf[DK], vf[DK];
-#pragma unroll
-  for (int dk = 0; dk < DK; ++dk) {
-    const uint32_t off = (uint32_t)(key * KROW + (2 * dk + lh) * 16);
-    kf[dk] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
-    vf[dk] = dk_role ? __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0) : u32x4{};
-  }
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-
-  const int nt = (N + BQ - 1) / BQ;
-  const int t0 = CAUSAL ? k_wg / BQ : 0;
-
-  u32x4 qst{}, dost{};
-  float lst = 0.f;
-  const int crow = tid / (D / 8), cch = tid % (D / 8);   // the chunk this thread copies
-  auto load = [&](int q0) {
-    if (tid < CH) {
-      const uint32_t off = (uint32_t)((q0 + crow) * KROW + cch * 16);
-      qst = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
-      dost = __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0);
-    }
-    if (tid >= T - 2 * BQ) {
-      const int r = tid - (T - 2 * BQ);
-      lst = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           r < BQ ? lser : dlr, (uint32_t)((q0 + (r % BQ)) * 4), 0, 0));
-    }
-  };
-  auto store = [&](int stg) {
-    uint8_t* base = smem + stg * STAGE;
-    if (tid < CH) {
-      const int off = crow * KROW + 16 * (cch ^ chunk_swizzle<D>(crow));
-      *(u32x4*)(base + off) = qst;
-      *(u32x4*)(base + TSZ + off) = dost;
-    }
-    if (tid >= T - 2 * BQ) {
-      const int r = tid - (T - 2 * BQ);
-      ((float*)(base + 2 * TSZ))[r] = r < BQ ? lst * kLog2e : lst;
-    }
-  };
-
-  const FragAddr<D> fa(lane);
-  const float c = a.c;
-
-  // one 32-query tile: S (and dP), then P or dS, then one product
-  // sb: the 32-query sub-block of the tile at st (its first query is q0)
-  auto compute = [&](const uint8_t* st, int sb, int q0, bool masked, auto role_tag) {
-    constexpr bool DKR = decltype(role_tag)::value;
-    const uint8_t* qt = st;
-    const uint8_t* dot = st + TSZ;
-    const float* l2 = (const float*)(st + 2 * TSZ) + 32 * sb;
-    const float* dl = l2 + (RING ? 64 : BQ);
-    const int r0 = 32 * sb;                  // first tile row of the sub-block
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-      s = E::mfma(fa.fread(qt, r0, dk), kf[dk], s);
-      if constexpr (DKR) dp = E::mfma(fa.fread(dot, r0, dk), vf[dk], dp);
-    }
-    u32x4 pk[2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 lq = *(const f32x4*)(l2 + 8 * g + 4 * lh);
-      if constexpr (RING) lq *= kLog2e;
-      f32x4 dq4 = f32x4{};
-      if constexpr (DKR) dq4 = *(const f32x4*)(dl + 8 * g + 4 * lh);
-      float val[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int r = 4 * g + b;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq[b]));
-        if (masked) {
-          const int q = q0 + 8 * g + 4 * lh + b;
-          const bool vis = q < N && (!CAUSAL || key <= q);
-          pv = vis ? pv : 0.f;
-        }
-        val[b] = DKR ? pv * (dp[r] - dq4[b]) : pv;
-      }
-      pk[g >> 1][2 * (g & 1)] = E::pack(val[0], val[1]);
-      pk[g >> 1][2 * (g & 1) + 1] = E::pack(val[2], val[3]);
-    }
-    // dV^T += dO^T P  or  dK^T += Q^T dS
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(DKR ? qt : dot, r0 + 16 * h, db), pk[h], acc[db]);
-  };
-
-  auto tile = [&](const uint8_t* st, int t) {
-#pragma unroll
-    for (int sb = 0; sb < SUB; ++sb) {
-      const int q0 = t * BQ + 32 * sb;
-      // every query of the sub-block precedes every key of the wave: nothing visible
-      const bool skip = CAUSAL && q0 + 31 < k_w;
-      if (!skip) {
-        const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < k_w + 31);
-        if (dk_role) compute(st, sb, q0, masked, std::true_type{});
-        else compute(st, sb, q0, masked, std::false_type{});
-      }
-    }
-  };
-
-  if constexpr (!RING) {
-    if (t0 < nt) {
-      load(t0 * BQ);
-      store(0);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      for (int t = t0; t < nt; ++t) {
-        const int stg = (t - t0) & 1;
-        if (t + 1 < nt) load((t + 1) * BQ);
-        tile(smem + stg * STAGE, t);
-        if (t + 1 < nt) store(stg ^ 1);
-        __syncthreads();
-      }
-    }
-  } else {
-    // Copy instructions of one tile: NI per tensor (Q, dO) of 1 KiB each,
-    // IPW per wave; waves 0 and 1 also copy the 64 LSE and D slots (4 bytes
-    // per lane; with 32-query tiles the slots past the tile are not read).
-    constexpr int NI = TSZ / 1024;
-    constexpr int IPW = 2 * NI / 8;
-    static_assert(2 * NI % 8 == 0 && IPW >= 1 && 3 * (IPW + 1) < 16, "tile copies must split evenly over the waves");
-    // the wave index read from lane 0, so that the copy's buffer descriptor
-    // and LDS destination (scalar operands) are known to be wave-uniform
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t dsrc[IPW];
-    int ddst[IPW];
-    bool dq_t[IPW];
-#pragma unroll
-    for (int k = 0; k < IPW; ++k) {
-      const int i = wv * IPW + k;                 // copy instruction index
-      dq_t[k] = i >= NI;                          // false: Q, true: dO
-      const int b = (i % NI) * 1024 + 16 * lane;  // byte of the tile this lane fills
-      const int row = b / KROW, phys = (b % KROW) / 16;
-      dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
-      ddst[k] = (dq_t[k] ? TSZ : 0) + (i % NI) * 1024;
-    }
-    const bool stat_wave = wv < 2;                // wave 0: LSE, wave 1: D
-    // The tile's offset is the copy's SGPR offset; the buffer range check
-    // covers the SGPR, VGPR and instruction offsets together (measured on
-    // gfx950), so rows past N read as zero.
-    auto dma = [&](int t, int stg) {
-      uint8_t* base = smem + stg * STAGE;
-      const int qoff = t * BQ * KROW;
-#pragma unroll
-      for (int k = 0; k < IPW; ++k) lds_dma16_asm(dq_t[k] ? dor : qr, base + ddst[k], dsrc[k], qoff);
-      if (stat_wave) lds_dma4_asm(wv == 0 ? lser : dlr, base + 2 * TSZ + (wv == 0 ? 0 : 256), (uint32_t)(4 * lane), t * BQ * 4);
-    };
-    // copies this wave issues per tile
-    auto wait_tile = [&](bool next_in_flight, bool next2_in_flight) {
-      // tiles issued after the one awaited: up to two (tiles t+1, t+2)
-      const int after = (next_in_flight ? 1 : 0) + (next2_in_flight ? 1 : 0);
-      if (stat_wave) {
-        if (after == 2) FA2_WAIT_VMCNT(2 * (IPW + 1));
-        else if (after == 1) FA2_WAIT_VMCNT(IPW + 1);
-        else FA2_WAIT_VMCNT(0);
-      } else {
-        if (after == 2) FA2_WAIT_VMCNT(2 * IPW);
-        else if (after == 1) FA2_WAIT_VMCNT(IPW);
-        else FA2_WAIT_VMCNT(0);
-      }
-    };
-    if (t0 < nt) {
-      // K, V fragments were loaded first; then tiles t0 .. t0+2
-      const int first = nt - t0 < 3 ? nt - t0 : 3;
-      for (int i = 0; i < first; ++i) dma(t0 + i, i);
-      // The fragment loads are older than every copy: they have landed once
-      // at most this wave's copies remain.  Passing the fragment registers
-      // through an empty statement here puts the compiler's own wait for
-      // them before the loop rather than inside it, where it would also
-      // drain the copies of the next tiles on every iteration.
-      const int per_tile = IPW + (stat_wave ? 1 : 0);
-      if (first * per_tile >= 3 * (IPW + 1)) FA2_WAIT_VMCNT(3 * (IPW + 1));
-      else if (first * per_tile >= 3 * IPW) FA2_WAIT_VMCNT(3 * IPW);
-      else if (first * per_tile >= 2 * (IPW + 1)) FA2_WAIT_VMCNT(2 * (IPW + 1));
-      else if (first * per_tile >= 2 * IPW) FA2_WAIT_VMCNT(2 * IPW);
-      else if (first * per_tile >= IPW + 1) FA2_WAIT_VMCNT(IPW + 1);
-      else if (first * per_tile >= IPW) FA2_WAIT_VMCNT(IPW);
-      else FA2_WAIT_VMCNT(0);
-#pragma unroll
-      for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(kf[dk]), "v"(vf[dk]));
-      for (int t = t0; t < nt; ++t) {
-        const int i = t - t0;
-        wait_tile(t + 1 < nt, t + 2 < nt);
-        // every wave's copies of tile t have landed and every wave is done
-        // with tile t-1, whose stage (i+3)%4 now receives tile t+3
-        __syncthreads();
-        if (t + 3 < nt) dma(t + 3, (i + 3) & 3);
-        tile(smem + (i & 3) * STAGE, t);
-      }
-    }
-  }
-
-  // ---- epilogue: dV = dV^T or dK = scale * dK^T, transposed back ----------
-  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((uint16_t*)(dk_role ? a.dk : a.dv) + head_off), 0, head_bytes, kBufferWord3);
-  const float sc = dk_role ? a.scale : 1.f;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 32 * db + 8 * i + 4 * lh;
-      u32x2 w;
-      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
-      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
-      __builtin_amdgcn_raw_buffer_store_b64(w, outr, (uint32_t)(key * KROW + d * 2), 0, 0);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dK, dV with P handed from one wave of a SIMD to the other: one workgroup per
 // (key block of 128 keys, head), 8 waves, two per SIMD; wave w owns keys
 // [k_wg + 32*(w%4), +32).  Query tiles of 64 rows (two 32-query sub-blocks),
@@ -879,7 +591,14 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
     }
   };
 
-  // ---- 3-stage ring of query tiles, two tiles ahead (as in the split kernel) --
+  // ---- 3-stage ring of query tiles, two tiles ahead ---------------------------
+  // Q, dO, LSE and D go straight from HBM into the ring (buffer_load ... lds
+  // issued as inline assembly, no staging registers); each wave waits for its
+  // own copies of a tile, then one barrier per tile publishes it and frees the
+  // stage of the previous tile.  The compiler does not see the copies (with
+  // the builtin it cannot tell the ring's stages apart and drains every copy
+  // in flight before each barrier); LSE stays in base e in LDS and is scaled
+  // by log2(e) when read.
   constexpr int NI = TSZ / 1024;
   constexpr int IPW = 2 * NI / 8;
   static_assert(2 * NI % 8 == 0 && IPW >= 1 && 2 * (IPW + 1) < 16, "tile copies must split evenly over the waves");
@@ -907,7 +626,9 @@ void fa2_bwd_dkdv_pair_kernel(BwdArgs a) {
   if (t0 < nt) {
     const int first = nt - t0 < 2 ? nt - t0 : 2;
     for (int i = 0; i < first; ++i) dma(t0 + i, i);
-    // fragment loads are older than every copy (see the split kernel)
+    // the fragment loads are older than every copy: they have landed once at
+    // most this wave's copies remain; the empty statements keep the
+    // compiler's own wait for them out of the loop
     const int per_tile = IPW + (stat_wave ? 1 : 0);
     if (first * per_tile >= 2 * (IPW + 1)) FA2_WAIT_VMCNT(2 * (IPW + 1));
     else if (first * per_tile >= 2 * IPW) FA2_WAIT_VMCNT(2 * IPW);
@@ -1180,7 +901,8 @@ void fa2_bwd_dkdv_pipe_kernel(BwdArgs a) {
   };
   if (t0 < nt) {
     dma(t0, 0);
-    // the fragment loads and tile t0 have landed (see the split kernel for the empty statement)
+    // the fragment loads and tile t0 have landed; the empty statements keep
+    // the compiler's own wait for the fragments out of the loop
     FA2_WAIT_VMCNT(0);
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(bf[dk]));
@@ -1217,18 +939,12 @@ void fa2_bwd_dkdv_pipe_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (query block of 32*NW queries, head), wave w owns
 // queries [q_wg + 32w, +32).  Key tiles of 64 rows: K and V (row-major,
-// swizzled) staged in LDS.  RING = false: two stages, register-staged copies
-// one tile ahead; RING = true: three stages filled straight from memory by
-// inline-assembly copies two tiles ahead (as in the dK/dV ring).
+// swizzled) staged in LDS, two stages, register-staged copies one tile
+// ahead.
 //
 // LOOK > 0: the MFMAs of each phase are issued in a fixed order with LOOK
 // operand reads ahead (scheduling-group barriers), as in the forward pass.
-// FUSED_D: the kernel computes D_i = dO_i . O_i itself from the dO row it
-// holds and the O row it loads (each lane half holds half of the row; one
-// exchange between lane l and l^32 completes the sum), uses it, and writes
-// it to delta for the dK/dV kernel, which then runs after this one; the
-// separate D kernel is not launched.
-template <bool BF16, int D, bool CAUSAL, class TL, bool RING = false, int LOOK = 0, bool FUSED_D = false>
+template <bool BF16, int D, bool CAUSAL, class TL, int LOOK = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(TL::THREADS, TL::THREADS),
                           amdgpu_waves_per_eu(TL::WPE, TL::WPE)))
 void fa2_bwd_dq_kernel(BwdArgs a) {
@@ -1239,10 +955,10 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
   constexpr int TSZ = BC * KROW;
   constexpr int STAGE = 2 * TSZ;
-  constexpr int NS = RING ? 3 : 2;
+  constexpr int NS = 2;
   constexpr int CH = BC * D / 8;
-  constexpr int CH_T = RING ? 1 : CH / T;
-  static_assert(RING || CH % T == 0, "tile copy must split evenly over threads");
+  constexpr int CH_T = CH / T;
+  static_assert(CH % T == 0, "tile copy must split evenly over threads");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1288,24 +1004,7 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
       (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
   const float lse2 =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lser, (uint32_t)(q * 4), 0, 0)) * kLog2e;
-  float dlt;
-  if constexpr (FUSED_D) {
-    const __amdgpu_buffer_rsrc_t orr = rsrc(a.o);
-    float part = 0.f;
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-      const u32x4 ov = __builtin_amdgcn_raw_buffer_load_b128(orr, (uint32_t)(q * KROW + (2 * dk + lh) * 16), 0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        part = __builtin_fmaf(half_lo<BF16>(ov[t]), half_lo<BF16>(dof[dk][t]), part);
-        part = __builtin_fmaf(half_hi<BF16>(ov[t]), half_hi<BF16>(dof[dk][t]), part);
-      }
-    }
-    dlt = sum_halves(part);
-    if (lh == 0) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dlt), dlr, (uint32_t)(q * 4), 0, 0);
-  } else {
-    dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
-  }
+  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
 
   f32x16 acc[DB];
 #pragma unroll
@@ -1421,275 +1120,14 @@ void fa2_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  if constexpr (!RING) {
-    load(0);
-    store(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-      if (j + 1 < nt) load((j + 1) * BC);
-      tile(smem + (j & 1) * STAGE, j);
-      if (j + 1 < nt) store((j + 1) & 1);
-      __syncthreads();
-    }
-  } else {
-    // NI copy instructions of 1 KiB per tensor and tile, IPW per wave
-    constexpr int NI = TSZ / 1024;
-    constexpr int IPW = 2 * NI / NW;
-    static_assert(2 * NI % NW == 0 && IPW >= 1 && IPW <= 7, "tile copies must split evenly over the waves");
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t dsrc[IPW];
-    int ddst[IPW];
-    bool isv[IPW];
-#pragma unroll
-    for (int k = 0; k < IPW; ++k) {
-      const int i = wv * IPW + k;
-      isv[k] = i >= NI;                           // false: K, true: V
-      const int b = (i % NI) * 1024 + 16 * lane;
-      const int row = b / KROW, phys = (b % KROW) / 16;
-      dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
-      ddst[k] = (isv[k] ? TSZ : 0) + (i % NI) * 1024;
-    }
-    // the tile's offset is the SGPR offset (range-checked with the rest: rows past N read as zero)
-    auto dma = [&](int j, int stg) {
-      uint8_t* base = smem + stg * STAGE;
-      const int koff = j * BC * KROW;
-#pragma unroll
-      for (int k = 0; k < IPW; ++k) lds_dma16_asm(isv[k] ? vr : kr, base + ddst[k], dsrc[k], koff);
-    };
-    const int first = nt < 2 ? nt : 2;
-    for (int i = 0; i < first; ++i) dma(i, i);
-    // Q, dO fragments, LSE and D were loaded before the copies: they have
-    // landed once at most this wave's copies remain; the empty statement
-    // keeps the compiler's own wait for them out of the loop
-    if (first == 2) FA2_WAIT_VMCNT(2 * IPW);
-    else FA2_WAIT_VMCNT(IPW);
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(qf[dk]), "v"(dof[dk]));
-    asm volatile("" ::"v"(lse2), "v"(dlt));
-    for (int j = 0; j < nt; ++j) {
-      // this wave's copies of tile j are done once only tile j+1's may remain
-      if (j + 1 < nt) FA2_WAIT_VMCNT(IPW);
-      else FA2_WAIT_VMCNT(0);
-      // every wave's tile j has landed and every wave is done with tile j-1,
-      // whose stage (j+2)%3 now receives tile j+2
-      __syncthreads();
-      if (j + 2 < nt) dma(j + 2, (j + 2) % 3);
-      tile(smem + (j % 3) * STAGE, j);
-    }
-  }
-
-  // ---- epilogue: dQ = scale * dQ^T (transposed back) ----------------------
-  const __amdgpu_buffer_rsrc_t dqr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((uint16_t*)a.dq + head_off), 0, head_bytes, kBufferWord3);
-  const float sc = a.scale;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 32 * db + 8 * i + 4 * lh;
-      u32x2 w;
-      w[0] = E::pack(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
-      w[1] = E::pack(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
-      __builtin_amdgcn_raw_buffer_store_b64(w, dqr, (uint32_t)(q * KROW + d * 2), 0, 0);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ pipelined across key tiles: the layout of fa2_bwd_dq_kernel (8 waves x
-// 32 queries, 64-key tiles), with the dQ^T += K^T dS^T product of tile j-1
-// issued at the start of iteration j from the packed dS^T kept in registers,
-// before the S^T and dP^T products of tile j, so each wave starts every
-// iteration with MFMAs that do not wait for that iteration's scores.  K and V
-// tiles j-1 .. j+2 are in a 4-stage LDS ring filled by inline-assembly copies
-// (tile j+2 issued at the start of iteration j, two tiles in flight); one
-// barrier per iteration.
-template <bool BF16, int D, bool CAUSAL, int LOOK = 4>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void fa2_bwd_dq_pipe_kernel(BwdArgs a) {
-  using E = Elem<BF16>;
-  constexpr int NW = 8, BR = 32 * NW;
-  constexpr int BC = 64;
-  constexpr int NKB = BC / 32;
-  constexpr int DK = D / 16, DB = D / 32, KROW = D * 2;
-  constexpr int TSZ = BC * KROW;
-  constexpr int STAGE = 2 * TSZ;
-  constexpr int NS = 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 31, lh = lane >> 5;
-
-  int bh, qblk;
-  {
-    const int i = blockIdx.x;
-    const int total = a.nblk * a.BH;
-    if constexpr (!CAUSAL) {
-      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
-      bh = logical / a.nblk;
-      qblk = logical % a.nblk;
-    } else {
-      bh = i % a.BH;
-      qblk = a.nblk - 1 - i / a.BH;
-    }
-  }
-  const int N = a.N;
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  auto rsrc = [&](const void* p) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p + head_off), 0, head_bytes, kBufferWord3);
-  };
-  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q), kr = rsrc(a.k), vr = rsrc(a.v), dor = rsrc(a.dout);
-
-  const int q_wg = qblk * BR;
-  const int q_w = q_wg + 32 * wave;
-  const int q = q_w + lr;
-
-  u32x4 qf[DK], dof[DK];
-#pragma unroll
-  for (int dk = 0; dk < DK; ++dk) {
-    const uint32_t off = (uint32_t)(q * KROW + (2 * dk + lh) * 16);
-    qf[dk] = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
-    dof[dk] = __builtin_amdgcn_raw_buffer_load_b128(dor, off, 0, 0);
-  }
-  const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t dlr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.delta + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-  const float lse2 =
-      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lser, (uint32_t)(q * 4), 0, 0)) * kLog2e;
-  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dlr, (uint32_t)(q * 4), 0, 0));
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-
-  int nt = (N + BC - 1) / BC;
-  if constexpr (CAUSAL) {
-    const int last_row = min(q_wg + BR, N) - 1;
-    nt = min(nt, last_row / BC + 1);
-  }
-  auto tile_skip = [&](int key0) { return CAUSAL && key0 > q_w + 31; };
-
-  const FragAddr<D> fa(lane);
-  const float c = a.c;
-  u32x4 dsp[NKB][2];    // packed dS^T of the previous tile
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    dsp[kb][0] = u32x4{};
-    dsp[kb][1] = u32x4{};
-  }
-
-  // tail of tile j (stage st): dQ^T += K^T dS^T
-  auto tail = [&](const uint8_t* st) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[db] = E::mfma(fa.tread(st, 32 * kb + 16 * h, db), dsp[kb][h], acc[db]);
-    if constexpr (LOOK > 0) {
-      constexpr int NM = DB * NKB * 2;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * LOOK, 0);
-#pragma unroll
-      for (int i = 0; i < NM - LOOK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, LOOK, 0);
-    }
-  };
-  // head of tile j (stage st): S^T, dP^T, then dS^T packed into dsp
-  auto head = [&](const uint8_t* st, int key0) {
-    const uint8_t* kt = st;
-    const uint8_t* vt = st + TSZ;
-    const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w);
-    f32x16 sv[NKB], dp[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sv[kb] = f32x16{};
-      dp[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sv[kb] = E::mfma(fa.fread(kt, 32 * kb, dk), qf[dk], sv[kb]);
-        dp[kb] = E::mfma(fa.fread(vt, 32 * kb, dk), dof[dk], dp[kb]);
-      }
-    }
-    if constexpr (LOOK > 0) {
-      constexpr int NM = 2 * NKB * DK;
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (i < NM - LOOK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][r], c, -lse2));
-        if (masked) {
-          const int kk = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const bool vis = kk < N && (!CAUSAL || kk <= q);
-          pv = vis ? pv : 0.f;
-        }
-        ds[r] = pv * (dp[kb][r] - dlt);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) dsp[kb][h][t] = E::pack(ds[8 * h + 2 * t], ds[8 * h + 2 * t + 1]);
-    }
-  };
-
-  // ---- 4-stage ring: K, V tiles j-1 .. j+2 -----------------------------------
-  constexpr int NI = TSZ / 1024;
-  constexpr int IPW = 2 * NI / NW;
-  static_assert(2 * NI % NW == 0 && IPW >= 1 && 2 * IPW < 16, "tile copies must split evenly over the waves");
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t dsrc[IPW];
-  int ddst[IPW];
-  bool isv[IPW];
-#pragma unroll
-  for (int k = 0; k < IPW; ++k) {
-    const int i = wv * IPW + k;
-    isv[k] = i >= NI;
-    const int b = (i % NI) * 1024 + 16 * lane;
-    const int row = b / KROW, phys = (b % KROW) / 16;
-    dsrc[k] = (uint32_t)(row * KROW + 16 * (phys ^ chunk_swizzle<D>(row)));
-    ddst[k] = (isv[k] ? TSZ : 0) + (i % NI) * 1024;
-  }
-  auto dma = [&](int j, int stg) {
-    uint8_t* base = smem + stg * STAGE;
-    const int koff = j * BC * KROW;
-#pragma unroll
-    for (int k = 0; k < IPW; ++k) lds_dma16_asm(isv[k] ? vr : kr, base + ddst[k], dsrc[k], koff);
-  };
-  dma(0, 0);
-  if (nt > 1) dma(1, 1);
-  // Q, dO fragments, LSE, D (loaded before the copies) and tile 0 have landed
-  // once at most tile 1's copies remain
-  if (nt > 1) FA2_WAIT_VMCNT(IPW);
-  else FA2_WAIT_VMCNT(0);
-#pragma unroll
-  for (int dk = 0; dk < DK; ++dk) asm volatile("" ::"v"(qf[dk]), "v"(dof[dk]));
-  asm volatile("" ::"v"(lse2), "v"(dlt));
+  load(0);
+  store(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  for (int j = 0; j <= nt; ++j) {
-    // stage (j+2)%4 held tile j-2, last used in iteration j-1
-    if (j + 2 < nt) dma(j + 2, (j + 2) % 4);
-    if (j >= 1 && !tile_skip((j - 1) * BC)) tail(smem + ((j + 3) % 4) * STAGE);
-    if (j < nt && !tile_skip(j * BC)) head(smem + (j % 4) * STAGE, j * BC);
-    // tile j+1 (issued one iteration earlier) must have landed for iteration
-    // j+1; tile j+2's copies may remain
-    if (j + 2 < nt) FA2_WAIT_VMCNT(IPW);
-    else FA2_WAIT_VMCNT(0);
+  for (int j = 0; j < nt; ++j) {
+    if (j + 1 < nt) load((j + 1) * BC);
+    tile(smem + (j & 1) * STAGE, j);
+    if (j + 1 < nt) store((j + 1) & 1);
     __syncthreads();
   }
 

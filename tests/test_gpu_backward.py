@@ -85,7 +85,7 @@ def run_case(what, B, H, N, d, dtype, causal, scale, seed, heads=None, sigma=1.0
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 31, 64, 65, 127, 129, 200, 513])
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
 def test_backward_edge_shapes(variant, N, d, causal, dtype):
     """Ragged N (partial query and key tiles, partial workgroups), single rows,
     for every dK/dV configuration."""
@@ -96,14 +96,14 @@ def test_backward_edge_shapes(variant, N, d, causal, dtype):
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
 def test_backward_scales(variant, scale, causal):
     """Zero and negative scales (P uniform over the visible keys; sign flips)."""
     run_case(f"v{variant} scale={scale} causal={causal}", 1, 2, 300, 128, "bf16", causal, scale, seed=31,
              variant=variant)
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
 def test_backward_batch_heads_layout(variant):
     """Several batches and heads in one launch: each head's gradients land in its own slab."""
     run_case(f"v{variant} B=3 H=5", 3, 5, 192, 64, "fp16", True, 0.125, seed=41, variant=variant)
