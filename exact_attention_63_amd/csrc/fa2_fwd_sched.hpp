@@ -132,10 +132,12 @@ __device__ __forceinline__ u32x32 sched_load_q(__amdgpu_buffer_rsrc_t qr, const 
   return q32;
 }
 
-// The assembly main loop over the item's full tiles (ntiles >= 1; K tiles
-// 0-2 and V tiles 0-1 in ring stages 0-2, every copy of them complete).  It
-// leaves the next item's tiles there in the same way when nx.has != 0, with
-// its Q fragments in q32 and its K and V descriptors in kr and vr.
+// The assembly main loop over the item's full tiles (ntiles >= 1).  Before
+// the first item, K tiles 0-2 and V tiles 0-1 are in ring stages 0-2 and
+// the workgroup has synchronised after every wave waited for its copies.
+// With nx.has != 0 the loop leaves the next item's tiles there (the next
+// loop's barriers publish them), its Q fragments in q32 and its K and V
+// descriptors in kr and vr; without, nx holds the current descriptors.
 template <bool BF16>
 __device__ __forceinline__ void sched_loop(f32x16& acc0, f32x16& acc1, f32x16& acc2, f32x16& acc3, float& m_run,
                                            float& l_run, u32x32& q32, __amdgpu_buffer_rsrc_t& kr,
@@ -170,7 +172,7 @@ __device__ __forceinline__ void sched_store(const Args& a, int bh, int q_w, int 
       (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
   const int row = q_w + lr;
   const float l = sum_halves(l_run);
-  const float inv = 1.f / l;
+  const float inv = __builtin_amdgcn_rcpf(l);   // l >= 1: the row's largest p is 1
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const f32x16& acc = db == 0 ? acc0 : db == 1 ? acc1 : db == 2 ? acc2 : acc3;
@@ -258,6 +260,7 @@ void fa2_fwd_sched_kernel(Args a) {
 
   if (nfull > 0) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
     const SchedNext none{kr, vr, qr, 0u, 0u};
     sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, nfull, none);
   }
@@ -388,6 +391,7 @@ void fa2_fwd_sched_persist_kernel(Args a) {
   const float c = c_neg ? -a.c : a.c;
   if (c_neg) q32 ^= 0x80008000u;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
 
   for (int i = 1;; ++i) {
     const int nxt = item(i);

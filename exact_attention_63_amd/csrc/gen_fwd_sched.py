@@ -91,7 +91,7 @@ S_KDESC, S_VDESC = 40, 44   # buffer descriptors of this head's K and V
 S_C = 48                # c = |scale| * log2(e)
 S_T = 49                # number of full tiles T >= 1
 S_J = 50                # interval counter j
-S_SOFF = 51             # byte offset of the tile being copied
+S_SOFF = 51             # byte offset (in its head) of the K tile this interval copies
 S_M0B = 52              # LDS address of this wave's 2 KiB share of a tile
 S_TM1 = 53              # T - 1
 S_J2 = 54               # j + 2
@@ -105,7 +105,8 @@ S_NKD, S_NVD, S_NQD = 56, 60, 64
 S_NQOFF = 68
 S_HASN = 69
 S_TMP = 70
-SGPR_CLOBBER = [S_J, S_SOFF, S_TM1, S_J2, S_J3, S_TMP]
+S_VSOFF = 71            # byte offset of the V tile this interval copies
+SGPR_CLOBBER = [S_J, S_SOFF, S_TM1, S_J2, S_J3, S_TMP, S_VSOFF]
 
 
 def vr(lo, n=1):
@@ -214,17 +215,17 @@ def softmax_pair(a, buf, q):
 def softmax_start(a):
     a(f"v_mov_b32 v{R_RS0}, 0")
     a(f"v_mov_b32 v{R_RS1}, 0")
-    a(f"v_mov_b32 v{R_ALPHA}, 1.0")
 
 
 def softmax_check(a, k):
     """Lane row sum; the exact-update path when any lane's sum exceeds the
-    bound (it returns to the instruction after the branch); then l."""
+    bound (it rescales acc and l itself and returns to the instruction after
+    the branch); then l += the row sum."""
     a(f"v_add_f32 v{R_T0}, v{R_RS0}, v{R_RS1}")
     a(f"v_cmp_lt_f32 vcc, 0x{THRESH:08x}, v{R_T0}")
     a(f"s_getpc_b64 s[{S_RET}:{S_RET + 1}]")
     a(f"s_cbranch_vccnz {a.lbl(f'exact{k}')}")
-    a(f"v_fma_f32 v{R_L}, v{R_L}, v{R_ALPHA}, v{R_T0}")
+    a(f"v_add_f32 v{R_L}, v{R_L}, v{R_T0}")
 
 
 def row_max(a, buf):
@@ -254,47 +255,39 @@ def rescale(a, name):
     a("s_nop 1")     # VALU write -> MFMA source read
 
 
-def dma_parts(a, k, name):
+def copy_setup(a):
+    """Descriptors and tile offsets of this interval's copies, without
+    branches.  Interval j copies K of tile j+3 and V of tile j+2.  Past the
+    item's last tile T-1 the same slots copy the next item's tiles 0-2 (K)
+    and 0-1 (V): at j+3 == T (j+2 == T) the K (V) descriptor becomes the
+    next item's, and tile t >= T is the next item's tile t - T (T % 4 == 0,
+    so it lands in the ring stage of its index).  Without a next item the
+    next descriptors are the current ones: the copies then fetch tiles 0-2
+    of the same head again into stages no wave reads, which keeps four
+    copies in every interval.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
+    for jr, cur, nxt, off in ((S_J3, S_KDESC, S_NKD, S_SOFF), (S_J2, S_VDESC, S_NVD, S_VSOFF)):
+        a(f"s_cmp_eq_u32 s{jr}, s{S_T}")
+        a(f"s_cselect_b64 s[{cur}:{cur + 1}], s[{nxt}:{nxt + 1}], s[{cur}:{cur + 1}]")
+        a(f"s_cselect_b64 s[{cur + 2}:{cur + 3}], s[{nxt + 2}:{nxt + 3}], s[{cur + 2}:{cur + 3}]")
+        a(f"s_cmp_lt_u32 s{jr}, s{S_T}")
+        a(f"s_cselect_b32 s{S_TMP}, 0, s{S_T}")
+        a(f"s_sub_u32 s{S_TMP}, s{jr}, s{S_TMP}")
+        a(f"s_lshl_b32 s{off}, s{S_TMP}, 14")
+
+
+def dma_parts(k):
     """The copies of interval j (j % 4 == k): K of tile j+3 into K stage
     (k+3) % 4 (last read by the scores of tile j-1 in interval j-2, or by
     the exact update of tile j-1 in interval j-1) and V of tile j+2 into V
     stage (k+2) % 4 (last read by P.V(j-2) in interval j-1), as four
     one-instruction pieces (this wave's two 1 KiB blocks of each).  K(j+3) is
-    first read in interval j+2, V(j+2) at the end of interval j+2.  Past the
-    item's last tile, the same slots copy the next item's K tiles 0-2 and V
-    tiles 0-1 (its tile t follows tile T - 1 in the ring, T % 4 == 0), so
-    that its loop finds them in stages 0-2.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
+    first read in interval j+2, V(j+2) at the end of interval j+2."""
     parts = []
-    for which, (jr, desc, base, nnext) in enumerate(((S_J3, S_KDESC, ((k + 3) % 4) * TSZ, 3),
-                                                     (S_J2, S_VDESC, VOFF + ((k + 2) % 4) * TSZ, 2))):
+    for desc, off, base in ((S_KDESC, S_SOFF, ((k + 3) % 4) * TSZ), (S_VDESC, S_VSOFF, VOFF + ((k + 2) % 4) * TSZ)):
         for kk in range(2):
-            cur = a.lbl(f"{name}c{which}{kk}c")
-            go = a.lbl(f"{name}c{which}{kk}g")
-            skip = a.lbl(f"{name}c{which}{kk}s")
-            parts.append([f"s_cmp_lt_u32 s{jr}, s{S_T}", f"s_cbranch_scc1 {cur}",
-                          f"s_cmp_eq_u32 s{S_HASN}, 0", f"s_cbranch_scc1 {skip}",
-                          f"s_sub_u32 s{S_TMP}, s{jr}, s{S_T}",
-                          f"s_cmp_lt_u32 s{S_TMP}, {nnext}", f"s_cbranch_scc0 {skip}",
-                          f"s_lshl_b32 s{S_SOFF}, s{S_TMP}, 14", f"s_branch {go}",
-                          f"{cur}:", f"s_lshl_b32 s{S_SOFF}, s{jr}, 14",
-                          f"{go}:", f"s_add_u32 m0, s{S_M0B}, {base + 1024 * kk}", "s_nop 0",
-                          f"buffer_load_dwordx4 {vr(R_DSRC + kk)}, s[{desc}:{desc + 3}], s{S_SOFF} offen lds",
-                          f"{skip}:"])
+            parts.append([f"s_add_u32 m0, s{S_M0B}, {base + 1024 * kk}", "s_nop 0",
+                          f"buffer_load_dwordx4 {vr(R_DSRC + kk)}, s[{desc}:{desc + 3}], s{off} offen lds"])
     return parts
-
-
-def switch_descriptors(a, name):
-    """Once the current item's K (V) copies are done -- from interval T - 3
-    (T - 2) on -- the K (V) descriptor becomes the next item's."""
-    for jr, cur, nxt in ((S_J3, S_KDESC, S_NKD), (S_J2, S_VDESC, S_NVD)):
-        lbl = a.lbl(f"{name}sw{cur}")
-        a(f"s_cmp_eq_u32 s{jr}, s{S_T}")
-        a(f"s_cbranch_scc0 {lbl}")
-        a(f"s_cmp_eq_u32 s{S_HASN}, 0")
-        a(f"s_cbranch_scc1 {lbl}")
-        a(f"s_mov_b64 s[{cur}:{cur + 1}], s[{nxt}:{nxt + 1}]")
-        a(f"s_mov_b64 s[{cur + 2}:{cur + 3}], s[{nxt + 2}:{nxt + 3}]")
-        a(f"{lbl}:")
 
 
 def load_next_q(a, name):
@@ -316,32 +309,23 @@ def dma_half(a, desc, base):
         a(f"buffer_load_dwordx4 {vr(R_DSRC + kk)}, s[{desc}:{desc + 3}], s{S_SOFF} offen lds")
 
 
-def end_interval(a, name):
+def end_interval(a):
     """Interval j+1 reads K(j+2) and V(j+1) (its last instructions prefetch
     V^T operands of P.V(j+1)), both copied in interval j-1: wait for this
-    wave's copies issued before interval j -- the four of interval j stay in
-    flight when it issued four (j + 3 < T, or a next item), else wait for
-    every copy -- then the barrier publishes them."""
-    a(f"s_add_u32 s{S_J3}, s{S_J}, 3")
-    a(f"s_cmp_lt_u32 s{S_J3}, s{S_T}")
-    a(f"s_cbranch_scc1 {a.lbl(name + 'w4')}")
-    a(f"s_cmp_eq_u32 s{S_HASN}, 0")
-    a(f"s_cbranch_scc1 {a.lbl(name + 'w0')}")
-    a(f"{a.lbl(name + 'w4')}:")
+    wave's copies issued before interval j (every interval issues four), then
+    the barrier publishes them."""
     a("s_waitcnt vmcnt(4)")
-    a(f"s_branch {a.lbl(name + 'wb')}")
-    a(f"{a.lbl(name + 'w0')}:")
-    a("s_waitcnt vmcnt(0)")
-    a(f"{a.lbl(name + 'wb')}:")
     a("s_barrier")
 
 
-def loop_control(a, k):
-    """j += 1; the next interval is the last one or another full one."""
+def loop_control(a, k, fall_through):
+    """j += 1; the next interval is the last one or another full one (the
+    next block in the layout when fall_through)."""
     a(f"s_add_u32 s{S_J}, s{S_J}, 1")
     a(f"s_cmp_eq_u32 s{S_J}, s{S_TM1}")
     a(f"s_cbranch_scc1 {a.lbl(f'last{(k + 1) % 4}')}")
-    a(f"s_branch {a.lbl(f'body{(k + 1) % 4}')}")
+    if not fall_through:
+        a(f"s_branch {a.lbl(f'body{(k + 1) % 4}')}")
 
 
 def score_phase(a, rd, stage, nbuf, first_keys_issued, after=None, look=LK):
@@ -485,13 +469,11 @@ def body(a, k, last, first):
     rd = Reads(a) if first else seeded_reads(a)
     a(f"s_add_u32 s{S_J2}, s{S_J}, 2")
     a(f"s_add_u32 s{S_J3}, s{S_J}, 3")
-    switch_descriptors(a, name)
+    copy_setup(a)
     # the copies go out one at a time, after MFMAs 2, 6, 10 and 14 of the
     # interval (all at once when it has no MFMA): issued back to back right
     # after the barrier by every wave, they measured 1-2 % slower
-    parts = dma_parts(a, k, name)
-    if not first:
-        rescale(a, name + "r")       # alpha still holds tile j-1's factor
+    parts = dma_parts(k)
     softmax_start(a)
     rounds = Rounds(a, cur, exact_max=last)
     nslots = (0 if first else 16) + (0 if last else 16)
@@ -522,11 +504,11 @@ def body(a, k, last, first):
     if not last:
         score_phase(a, rd, (k + 1) % 4, nxt, not first, after_mfma)
     if nslots == 0:
+        if last:
+            load_next_q(a, name)     # before the copies: the end waits for all but four
         for part in parts:
             for ins in part:
                 a(ins)
-        if last:
-            load_next_q(a, name)
     rounds.finish()
     if last:
         # reference from the exact row max: p <= 1, no check, no exact update
@@ -536,11 +518,12 @@ def body(a, k, last, first):
         softmax_check(a, k)
     # P.V(j) opens the next interval (or follows the last one)
     v_prefetch(Reads(a, vstart=V_START_LAST if last else 0), k)
-    end_interval(a, name)
+    end_interval(a)
     if last:
         a(f"s_branch {a.lbl(f'exit{k}')}")
     else:
-        loop_control(a, k)
+        # bodies 0-3 are laid out in order: 0-2 fall through to the next
+        loop_control(a, k, fall_through=not first and k < 3)
 
 
 def exit_pv(a, k):
@@ -555,8 +538,8 @@ def exit_pv(a, k):
 def exact_update(a, k):
     """Out-of-line exact update for the tile in stage k (score buffer k % 2):
     recompute S from K (still in LDS), m_new = max(m, max S c),
-    alpha = 2^(m - m_new), p = 2^(S c - m_new); returns with the lane row sum
-    in v{R_T0}."""
+    alpha = 2^(m - m_new), p = 2^(S c - m_new), acc and l times alpha;
+    returns with the lane row sum in v{R_T0}."""
     a.label(f"exact{k}")
     buf = k % 2
     score_phase(a, Reads(a), k, buf, False, look=LK_EXACT)
@@ -570,20 +553,25 @@ def exact_update(a, k):
     for q in range(16):
         softmax_pair(a, buf, q)
     a(f"v_add_f32 v{R_T0}, v{R_RS0}, v{R_RS1}")
+    # acc and l to the new reference (this interval's P.V MFMAs, which write
+    # acc, were issued 32 MFMAs ago)
+    a(f"v_mul_f32 v{R_L}, v{R_L}, v{R_ALPHA}")
+    for r in range(R_ACC, R_ACC + 16 * DB):
+        a(f"v_mul_f32 v{r}, v{r}, v{R_ALPHA}")
     a(f"s_add_u32 s{S_RET}, s{S_RET}, 4")       # past the s_cbranch_vccnz (4 bytes)
     a(f"s_addc_u32 s{S_RET + 1}, s{S_RET + 1}, 0")
     a(f"s_setpc_b64 s[{S_RET}:{S_RET + 1}]")
 
 
 def prologue(a):
-    """K of tiles 0-2 and V of tiles 0-1 are in stages 0-2 (copied by the C++
-    side, which waited for them, or by the previous item's last intervals,
-    waited for at the end of its block): publish them, S(0) into buffer 0,
-    m = exact row max of tile 0.  (No vmcnt wait here: the stores of the
-    previous item's output may still be in flight.)"""
+    """K of tiles 0-2 and V of tiles 0-1 are in stages 0-2: copied by the C++
+    side, which waited for them and synchronised the workgroup, or by the
+    previous item's last three intervals, whose barriers published all but
+    K of tile 2 and V of tile 1 (published by this item's first barrier,
+    before their first reads).  S(0) into buffer 0, m = exact row max of
+    tile 0."""
     a(f"s_mov_b32 s{S_J}, 0")
     a(f"s_add_u32 s{S_TM1}, s{S_T}, -1")
-    a("s_barrier")
     score_phase(a, Reads(a, kstart=K_START_PROLOGUE), 0, 0, False)
     a(f"v_mov_b32 v{R_L}, 0")
     a("s_nop 7")
@@ -609,7 +597,15 @@ def block(dtype):
     for k in range(4):
         exact_update(a, k)
     a(f"{a.lbl('done')}:")
-    a("s_waitcnt vmcnt(0) lgkmcnt(0)")   # the next item's Q and copies have landed
+    # The next item's Q landed before the last barrier (the last interval
+    # waited for every load but its four copies, which the next item's first
+    # interval waits for).  Without a next item, wait for those copies: the
+    # code after the block may reuse their stages.
+    a(f"s_cmp_eq_u32 s{S_HASN}, 0")
+    a(f"s_cbranch_scc0 {a.lbl('dn')}")
+    a("s_waitcnt vmcnt(0)")
+    a(f"{a.lbl('dn')}:")
+    a("s_waitcnt lgkmcnt(0)")
     a("s_nop 7")
     a("s_nop 7")     # MFMA results -> the C++ code that reads acc
     return a.lines

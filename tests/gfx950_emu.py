@@ -275,6 +275,12 @@ class Wave:
             dlo, _ = srange(args[0])
             slo, _ = srange(args[1])
             self.s[dlo], self.s[dlo + 1] = self.s[slo], self.s[slo + 1]
+        elif op == "s_cselect_b32":
+            self.sset(args[0], self.ssrc(args[1]) if self.scc else self.ssrc(args[2]))
+        elif op == "s_cselect_b64":
+            dlo, _ = srange(args[0])
+            slo, _ = srange(args[1] if self.scc else args[2])
+            self.s[dlo], self.s[dlo + 1] = self.s[slo], self.s[slo + 1]
         elif op == "s_sub_u32":
             r = self.ssrc(args[1]) - self.ssrc(args[2])
             self.scc = r < 0
@@ -530,7 +536,11 @@ class Wave:
 class Emulator:
     """texts: the program of every wave of the workgroup."""
 
-    def __init__(self, texts, lds_size, buffers, max_steps=200000):
+    def __init__(self, texts, lds_size, buffers, max_steps=200000, copies_may_continue=False):
+        """copies_may_continue: a program may end with global->LDS copies in
+        flight (the next program waits for them); they are completed at the
+        end of the run."""
+        self.copies_may_continue = copies_may_continue
         progs = {}
         for t in texts:
             if t not in progs:
@@ -591,6 +601,7 @@ class Emulator:
                 w.at_barrier = False
             self.phase += 1
         for w in self.waves:
-            if w.lds_q or w.vm_q:
+            if w.lds_q or any("regs" in c for c in w.vm_q) or (w.vm_q and not self.copies_may_continue):
                 raise EmuError(f"wave {w.wid} ends with loads in flight")
+            w.complete_vm(0)
         return self.waves

@@ -76,6 +76,10 @@ def init_wave(w, wave, qbits, N, qblk, T, c):
     wave.s[GEN.S_C] = int(np.float32(c).view(np.uint32))
     wave.s[GEN.S_T] = T
     wave.s[GEN.S_M0B] = 2048 * w
+    # no next item: its descriptors are the current ones
+    wave.s[GEN.S_NKD] = 1
+    wave.s[GEN.S_NVD] = 2
+    wave.s[GEN.S_HASN] = 0
 
 
 def run_workgroup(dtype, q, k, v, qblk, T, scale, text=None, hits=None):
@@ -238,7 +242,7 @@ def test_consecutive_items(dtype):
     text = "\n".join(GEN.block(dt))
     state = None
     for i, (h, qblk) in enumerate(items):
-        emu = Emulator([text] * 8, 128 * 1024, buffers)
+        emu = Emulator([text] * 8, 128 * 1024, buffers, copies_may_continue=i + 1 < len(items))
         for w, wave in enumerate(emu.waves):
             init_wave(w, wave, bits[h][0], N, qblk, T, c)
             if state is not None:                 # the previous block's registers and LDS
@@ -247,7 +251,10 @@ def test_consecutive_items(dtype):
             wave.v[GEN.R_QOFF] = (lanes % 32) * 256 + 16 * (lanes // 32)
             _desc(wave.s, GEN.S_KDESC, 11 + 3 * h, N * 256)
             _desc(wave.s, GEN.S_VDESC, 12 + 3 * h, N * 256)
-            if i + 1 < len(items):
+            if i + 1 == len(items):
+                _desc(wave.s, GEN.S_NKD, 11 + 3 * h, N * 256)
+                _desc(wave.s, GEN.S_NVD, 12 + 3 * h, N * 256)
+            else:
                 hn, qn = items[i + 1]
                 _desc(wave.s, GEN.S_NKD, 11 + 3 * hn, N * 256)
                 _desc(wave.s, GEN.S_NVD, 12 + 3 * hn, N * 256)
