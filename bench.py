@@ -33,18 +33,21 @@ METRIC = "attention fwd TFLOPS (and % of MFMA peak) at N=2048,d=128 bf16"
 BWD_METRIC = "attention bwd TFLOPS (and % of MFMA peak), 10*B*H*N^2*d FLOPs per call"
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}   # MI355X dense MFMA peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_fwd_kernel.hpp")
+CSRC = os.path.join(ROOT, "exact_attention_63_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_sched.hpp", "fa2_fwd_sched.inc")]
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
 
 
 def kernel_identity(w, variant: int = 0) -> str:
-    """Hash of the kernel template source and the tile configuration that the
+    """Hash of the forward kernel sources and the tile configuration that the
     workload runs with: the counters recorded for one identity are only reused
     for exactly that kernel."""
     import exact_attention_63_amd as fa2
     vi = variant or fa2.default_variant(0 if w.dtype == "fp16" else 1, w.d, w.causal)
     h = hashlib.sha256()
-    with open(KERNEL_SOURCE, "rb") as f:
-        h.update(f.read())
+    for src in KERNEL_SOURCES:
+        with open(src, "rb") as f:
+            h.update(f.read())
     h.update(fa2.variant_name(vi).encode())
     h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
     return h.hexdigest()[:16]
@@ -98,16 +101,54 @@ def per_call_stats(fn, calls: int):
             "p90_ms": round(t[min(len(t) - 1, int(0.9 * len(t)))], 5)}
 
 
+def host_info():
+    """Host cores this process may run on, the BLAS thread count and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return cores, blas, model
+
+
+def mfma_probe(iters: int = 100000):
+    """Sustained dense bf16 MFMA throughput (TFLOP/s) and shader clock (GHz)
+    measured now by bench_probe.so (an MFMA-only loop on every CU), or None
+    when the probe is not built."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fa2_probe_mfma.restype = ctypes.c_int
+    lib.fa2_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_double)]
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    rc = lib.fa2_probe_mfma(iters, torch.cuda.current_stream().cuda_stream, ctypes.byref(tf), ctypes.byref(ghz))
+    if rc != 0:
+        raise RuntimeError(f"fa2_probe_mfma failed with HIP error {rc}")
+    return {"value": round(tf.value, 1), "unit": "TFLOP/s", "clock_ghz": round(ghz.value, 3),
+            "what": "bench_probe.hip: back-to-back v_mfma_f32_32x32x16_bf16, 2 waves per SIMD on every CU, "
+                    "random operands, run right after the timed region"}
+
+
 def cpu_baseline(w, budget_s: float = 20.0):
     """The fp64 CPU oracle timed on whole heads of the same workload (in order)
     until about budget_s seconds of work are done or every head is done."""
     import oracle
     from workloads import workload_inputs, to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    host_cores, blas, model = host_info()
+    cores = min(blas, host_cores)
     q, k, v = workload_inputs(w)
     nh = w.B * w.H
     heads = 0
@@ -121,7 +162,7 @@ def cpu_baseline(w, budget_s: float = 20.0):
     dt = time.perf_counter() - t0
     flops_per_head = w.flops / nh
     return {"value": round(heads * flops_per_head / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
-            "kind": "oracle",
+            "host_cores": host_cores, "blas_threads": blas, "cpu_model": model, "kind": "oracle",
             "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, fp64 NumPy "
                       f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
@@ -168,11 +209,8 @@ def cpu_baseline_bwd(w, budget_s: float = 20.0):
     """The fp64 CPU gradient oracle timed on whole heads of the same workload."""
     import oracle
     from workloads import workload_grad_output, workload_inputs, to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    host_cores, blas, model = host_info()
+    cores = min(blas, host_cores)
     q, k, v = workload_inputs(w)
     do = workload_grad_output(w)
     nh = w.B * w.H
@@ -187,7 +225,7 @@ def cpu_baseline_bwd(w, budget_s: float = 20.0):
             break
     dt = time.perf_counter() - t0
     return {"value": round(heads * (w.bwd_flops / nh) / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
-            "kind": "oracle",
+            "host_cores": host_cores, "blas_threads": blas, "cpu_model": model, "kind": "oracle",
             "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, fp64 NumPy gradient "
                       f"oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
 
@@ -354,6 +392,10 @@ def main():
             "traffic": traffic,
         },
     }
+    probe = mfma_probe()
+    if probe is not None:
+        line["roofline"]["probe_peak"] = probe
+        line["roofline"]["frac_probe"] = round(tflops / probe["value"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -45,6 +45,26 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile bench.py's measurement probe (bench_probe.hip -> bench_probe.so,
+    beside bench.py); it is not part of the library."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode} on {PROBE_SRC}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
@@ -70,3 +90,4 @@ def build(verbose: bool = False) -> str:
 if __name__ == "__main__":
     path = build(verbose="--verbose" in sys.argv)
     print(path)
+    print(build_probe(verbose="--verbose" in sys.argv))
