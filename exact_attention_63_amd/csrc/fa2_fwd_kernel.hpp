@@ -186,6 +186,28 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Causal grids: workgroup i -> (head bh, query block qblk), heaviest query
+// blocks first.  Workgroups are dealt to the 8 XCDs round robin (workgroup i
+// runs on XCD i % 8), and with B*H a multiple of 8 the heads h with
+// h % 8 == x all run on XCD x.  With at least 64 query blocks per head (twice
+// the 32 CUs of an XCD), XCD x takes its heads one after the other, each
+// heaviest block first: the workgroups it runs at a time then belong to one
+// or two heads and share their K and V in its L2 (N = 16384: 2.9x fewer L2
+// misses).  With fewer blocks per head one head cannot fill an XCD, and
+// taking a head's light blocks before the next head's heavy ones leaves
+// heavy blocks for the end (N = 4096: 15 % slower), so the blocks of all
+// heads go level by level, heaviest first.
+__device__ __forceinline__ void causal_item(int i, int BH, int nqb, int& bh, int& qblk) {
+  if (BH % 8 == 0 && nqb >= 64) {
+    const int s = i / 8;                 // the s-th workgroup of XCD i % 8
+    bh = (s / nqb) * 8 + i % 8;
+    qblk = nqb - 1 - s % nqb;
+  } else {
+    bh = i % BH;
+    qblk = nqb - 1 - i / BH;
+  }
+}
+
 struct Args {
   const void* q;
   const void* k;
@@ -254,8 +276,8 @@ void fa2_fwd_kernel(Args a) {
   // Non-causal: all workgroups do equal work; consecutive logical ids walk the
   // query blocks of one head and are kept on one XCD (workgroups are dealt to
   // the 8 XCDs round-robin), so a head's K/V stay in that XCD's L2.
-  // Causal: heaviest query blocks first; with B*H a multiple of 8 each XCD
-  // then owns a fixed set of heads.
+  // Causal: causal_item (heaviest query blocks first, a head's blocks on one
+  // XCD).
   int bh, qblk;
   {
     const int i = blockIdx.x;
@@ -265,8 +287,7 @@ void fa2_fwd_kernel(Args a) {
       bh = logical / a.nqb;
       qblk = logical % a.nqb;
     } else {
-      bh = i % a.BH;
-      qblk = a.nqb - 1 - i / a.BH;
+      causal_item(i, a.BH, a.nqb, bh, qblk);
     }
   }
   const int N = a.N;

@@ -224,8 +224,7 @@ void fa2_fwd_sched_kernel(Args a) {
       bh = logical / a.nqb;
       qblk = logical % a.nqb;
     } else {
-      bh = i % a.BH;
-      qblk = a.nqb - 1 - i / a.BH;
+      causal_item(i, a.BH, a.nqb, bh, qblk);
     }
   }
   const int N = a.N;
