@@ -186,22 +186,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Causal grids: workgroup i -> (head bh, query block qblk), heaviest query
-// blocks first.  Workgroups are dealt to the 8 XCDs round robin (workgroup i
-// runs on XCD i % 8), and with B*H a multiple of 8 the heads h with
-// h % 8 == x all run on XCD x.  With at least 64 query blocks per head (twice
-// the 32 CUs of an XCD), XCD x takes its heads one after the other, each
-// heaviest block first: the workgroups it runs at a time then belong to one
-// or two heads and share their K and V in its L2 (N = 16384: 2.9x fewer L2
-// misses).  With fewer blocks per head one head cannot fill an XCD, and
-// taking a head's light blocks before the next head's heavy ones leaves
-// heavy blocks for the end (N = 4096: 15 % slower), so the blocks of all
-// heads go level by level, heaviest first.
+// Causal grids: workgroup i -> (head bh, query block qblk).  Workgroups are
+// dealt to the 8 XCDs round robin (workgroup i runs on XCD i % 8), so with
+// B*H a multiple of 8 the heads h with h % 8 == x all run on XCD x.  XCD x
+// takes them in groups of G heads, G = 32 / (query blocks per head) (at
+// least 1): about one block per CU of the XCD (32).  Within a group the
+// blocks go level by level, heaviest first.  The first group's blocks start
+// together, and as they finish (lightest first) the next group's blocks
+// start heaviest first, so every CU's total comes out about the same; the
+// workgroups an XCD runs at a time belong to one or two groups and share
+// their K and V in its L2 (N = 16384: 2.9x fewer L2 misses than all heads
+// of an XCD level by level).  Otherwise all heads go level by level.
 __device__ __forceinline__ void causal_item(int i, int BH, int nqb, int& bh, int& qblk) {
-  if (BH % 8 == 0 && nqb >= 64) {
+  const int G = nqb >= 32 ? 1 : 32 / nqb;
+  if (BH % 8 == 0 && (BH / 8) % G == 0) {
     const int s = i / 8;                 // the s-th workgroup of XCD i % 8
-    bh = (s / nqb) * 8 + i % 8;
-    qblk = nqb - 1 - s % nqb;
+    const int per = G * nqb;             // blocks of one group
+    const int g = s / per, r = s % per;
+    bh = (g * G + r % G) * 8 + i % 8;
+    qblk = nqb - 1 - r / G;
   } else {
     bh = i % BH;
     qblk = nqb - 1 - i / BH;
