@@ -1,9 +1,12 @@
 """The seeded input recipe: shapes, determinism, rounding and the key offset."""
 
+import math
+
 import numpy as np
 import torch
 
 import workloads
+import workloads as W
 from workloads import WORKLOADS, make_inputs, to_f64
 
 
@@ -52,3 +55,27 @@ def test_key_offset_is_per_key_row():
     assert np.all(np.abs(row_mean) <= 4.1)
     assert np.max(np.abs(diff - row_mean)) < 0.05
     assert row_mean.std() > 1.0
+
+
+def test_fp8_inputs_recipe():
+    (q8, k8, v8), (dq, dk, dv) = W.make_inputs_fp8(2, 3, 40, 64, seed=4)
+    q, k, v = W.make_inputs(2, 3, 40, 64, "bf16", seed=4)
+    for codes, desc, x16 in ((q8, dq, q), (k8, dk, k), (v8, dv, v)):
+        assert codes.dtype == torch.uint8 and codes.shape == (2, 3, 40, 64) and codes.is_contiguous()
+        assert ((codes & 0x7F) != 0x7F).all()                    # no NaN codes
+        # the codes decode (PyTorch) to the float32 draws within E4M3 rounding
+        back = codes.view(torch.float8_e4m3fn).double() * desc
+        assert torch.allclose(back, x16.double(), rtol=2 ** -4 + 2 ** -8, atol=2 ** -9 * desc)
+    again = W.make_inputs_fp8(2, 3, 40, 64, seed=4)
+    assert all(torch.equal(a, b) for a, b in zip(again[0], (q8, k8, v8))) and again[1] == (dq, dk, dv)
+
+
+def test_fp8_exact_inputs_recipe():
+    (q8, k8, v8), (dq, dk, dv), scale = W.make_exact_fp8(1, 2, 100, 128, seed=6)
+    assert (dq, dk) == (0.5, 0.25)
+    assert set(q8.unique().tolist()) <= {0x00, 0x38, 0xB8} and set(k8.unique().tolist()) <= {0x00, 0x38, 0xB8}
+    assert ((q8 != 0).sum(-1) == 8).all() and ((k8 != 0).sum(-1) == 16).all()
+    q = q8.view(torch.float8_e4m3fn).double() * dq
+    k = k8.view(torch.float8_e4m3fn).double() * dk
+    t = scale * (q @ k.transpose(-1, -2)) / math.log(2.0)
+    assert (t - t.round()).abs().max() < 1e-12 and t.abs().max() <= 8
