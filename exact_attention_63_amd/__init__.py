@@ -8,6 +8,7 @@ fallback: when the library is missing or no GPU is present, calls raise.
     from exact_attention_63_amd import forward
     o, lse = forward(q, k, v, causal=False)        # q, k, v: [B, H, N, d] cuda fp16/bf16
     dq, dk, dv, delta = backward(q, k, v, o, lse, do, causal=False)
+    o, lse = forward_fp8(q8, k8, v8, dq, dk, dv)    # E4M3 codes (uint8) and descales
 """
 
 from __future__ import annotations
@@ -17,7 +18,7 @@ import math
 import os
 
 __all__ = [
-    "forward", "backward", "bwd_num_variants", "bwd_variant_name", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "forward", "forward_fp8", "backward", "bwd_num_variants", "bwd_variant_name", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
     "default_variant",
     "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
     "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
@@ -50,6 +51,8 @@ EXPORTS = {
     "fa2_fwd": (_I, _FWD12 + [_I]),
     "fa2_fwd_variant": (_I, _FWD12 + [_I, _I]),
     "fa2_fwd_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+    "fa2_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
+    "fa2_fwd_fp8_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F]),
     "fa2_bwd": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P, _I]),
     "fa2_bwd_fp16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
     "fa2_bwd_bf16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
@@ -185,6 +188,56 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
                                    stream, code, int(variant))
     if rc != FA2_OK:
         raise Fa2Error(rc, "fa2_fwd_variant")
+    return out, lse
+
+
+def forward_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causal: bool = False,
+                scale: float | None = None, *, out=None, lse=None):
+    """FP8 attention forward: returns (O [B,H,N,d] bfloat16, LSE [B,H,N] float32).
+
+    q, k, v: contiguous CUDA (ROCm) uint8 tensors [B, H, N, d] of OCP E4M3
+    codes (a float8_e4m3fn tensor viewed as uint8), d in {64, 128}; the
+    inputs are decode(q) * descale_q etc.  scale defaults to 1/sqrt(d).
+    Enqueued on the current stream of q's device; the call does not
+    synchronise.  An empty problem returns the empty outputs without a
+    library call.
+    """
+    import torch
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one shape [B, H, N, d]; got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must hold E4M3 codes as uint8, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    if out.numel() == 0:
+        if d not in (64, 128):
+            raise Fa2Error(FA2_ERR_UNSUPPORTED, "head dimension")
+        return out, lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib().fa2_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, int(bool(causal)), float(scale), float(descale_q),
+                               float(descale_k), float(descale_v), stream)
+    if rc != FA2_OK:
+        raise Fa2Error(rc, "fa2_fwd_fp8")
     return out, lse
 
 

@@ -16,6 +16,7 @@
 #include "fa2_bwd_kernel.hpp"
 #include "fa2_fwd_roles.hpp"
 #include "fa2_fwd_sched.hpp"
+#include "fa2_fwd_fp8.hpp"
 
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -204,6 +205,65 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return FA2_OK;
 }
 
+
+// ---- FP8 forward ------------------------------------------------------------
+
+typedef void (*fp8_fn)(fa2::Fp8Args);
+const fp8_fn kFp8[2][2] = {{fa2::fa2_fwd_fp8_kernel<64, false>, fa2::fa2_fwd_fp8_kernel<64, true>},
+                           {fa2::fa2_fwd_fp8_kernel<128, false>, fa2::fa2_fwd_fp8_kernel<128, true>}};
+
+// c = scale * descale_q * descale_k * log2(e), in double, then float
+float fp8_exponent_scale(float scale, float dq, float dk) {
+  return (float)((double)scale * (double)dq * (double)dk * 1.4426950408889634);
+}
+
+int check_fp8(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+              int N, int d, int causal, float scale, float dq, float dk, float dv) {
+  if (causal != 0 && causal != 1) return FA2_ERR_ARG;
+  if (!finite_bits(scale) || !finite_bits(dq) || !finite_bits(dk) || !finite_bits(dv)) return FA2_ERR_ARG;
+  if (!finite_bits(fp8_exponent_scale(scale, dq, dk))) return FA2_ERR_ARG;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  // one head of o (2-byte elements) must be addressable with 32-bit byte offsets
+  if ((uint64_t)N * (uint64_t)d * 2u >= (1ull << 32)) return FA2_ERR_SHAPE;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  if (bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  const uint64_t elems = bh * (uint64_t)N * (uint64_t)d;
+  if (elems >= (1ull << 62)) return FA2_ERR_SHAPE;
+  if (((uint64_t)N + fa2::kFp8Rows - 1) / fa2::kFp8Rows * bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u)
+    return FA2_ERR_ALIGN;
+  const size_t ib = (size_t)elems;         // one byte per input element
+  const size_t ob = (size_t)elems * 2u;    // bf16 output
+  const size_t lb = (size_t)(bh * (uint64_t)N) * 4u;
+  if (overlaps(o, ob, q, ib) || overlaps(o, ob, k, ib) || overlaps(o, ob, v, ib) || overlaps(o, ob, lse, lb) ||
+      overlaps(lse, lb, q, ib) || overlaps(lse, lb, k, ib) || overlaps(lse, lb, v, ib))
+    return FA2_ERR_ALIAS;
+  return FA2_OK;
+}
+
+int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+            int causal, float scale, float dq, float dk, float dv, hipStream_t stream) {
+  const int st = check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv);
+  if (st != FA2_OK) return st;
+  const uint64_t bh = (uint64_t)B * (uint64_t)H;
+  fa2::Fp8Args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = (int)bh;
+  a.N = N;
+  a.nqb = (N + fa2::kFp8Rows - 1) / fa2::kFp8Rows;
+  a.c = fp8_exponent_scale(scale, dq, dk);
+  a.dv = dv;
+  const uint64_t blocks = (uint64_t)a.nqb * bh;
+  hipLaunchKernelGGL(kFp8[d == 128][causal], dim3((unsigned)blocks), dim3(512), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
+  return FA2_OK;
+}
 
 // ---- backward ---------------------------------------------------------------
 
@@ -415,6 +475,18 @@ FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const 
                              const float* lse, int B, int H, int N, int d, int causal,
                              float scale, int dtype, int variant) {
   return check(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, variant);
+}
+
+FA2_EXPORT int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int N, int d, int causal, float scale, float descale_q, float descale_k,
+                           float descale_v, hipStream_t stream) {
+  return run_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, stream);
+}
+
+FA2_EXPORT int fa2_fwd_fp8_check(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, int B, int H, int N, int d, int causal, float scale,
+                                 float descale_q, float descale_k, float descale_v) {
+  return check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v);
 }
 
 FA2_EXPORT int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -119,6 +119,49 @@ int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, co
                   int B, int H, int N, int d, int causal, float scale, int dtype, int variant);
 
 /*
+ * fa2_fwd_fp8 -- the forward pass with FP8 inputs.
+ *
+ * The pages name FP8 arithmetic as a hardware capability that v2 leaves
+ * unused ("FlashAttention v2 better parallelism + work partitioning"
+ * diagram, panel on what v2 changes) but give no FP8 scheme; this one is:
+ *
+ *   q, k, v  [in]  device, [B,H,N,d] 8-bit codes in the OCP E4M3 format
+ *                  (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *                  largest finite magnitude 448; S.1111.111 is NaN),
+ *                  16-byte aligned.  The inputs are decode(q) * descale_q,
+ *                  decode(k) * descale_k and decode(v) * descale_v.
+ *   o        [out] device, [B,H,N,d] bf16 (round to nearest even), 16-byte
+ *                  aligned, must not overlap any other argument
+ *   lse      [out] device, [B,H,N] float32, 16-byte aligned, must not
+ *                  overlap q, k, v or o
+ *   B, H, N, d, causal, scale, stream: as for fa2_fwd_fp16; N*d*2 bytes
+ *                  (one head of o) must stay below 2^32
+ *   descale_q, descale_k, descale_v: finite float32 factors, one per tensor
+ *
+ * O and LSE are those of the definition at the top of this file applied to
+ * the dequantised inputs, except for one rounding step: the probabilities
+ * enter the P.V product as E4M3 values.  Per tile of 8192/d keys (64 keys at
+ * d = 128, 128 at d = 64, in key order) and per row, P = 2^(8 + c*s - m)
+ * with c = scale * descale_q * descale_k * log2(e) and m the row's
+ * reference max, which moves to the tile's max only when that exceeds it
+ * by more than 0.75, is rounded to the nearest E4M3 value (ties to even);
+ * the row sum l takes the unrounded P.  Both products accumulate in fp32.
+ * Errors: as for fa2_fwd; scale, any descale, or c not finite in float32
+ * is FA2_ERR_ARG.
+ */
+int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, int causal, float scale,
+                float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/*
+ * fa2_fwd_fp8_check -- run exactly the argument validation of fa2_fwd_fp8 and
+ * return its status, without launching anything or calling the HIP runtime.
+ */
+int fa2_fwd_fp8_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      int B, int H, int N, int d, int causal, float scale,
+                      float descale_q, float descale_k, float descale_v);
+
+/*
  * fa2_bwd -- the backward pass: gradients of the forward pass's O with
  * respect to q, k and v, given the upstream gradient dO.
  *
@@ -145,8 +188,7 @@ int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, co
  *
  * Every pointer is 16-byte aligned and owned by the caller; no output may
  * overlap an input or another output.  The call enqueues three kernels on
- * stream (D, then dK and dV, then dQ; variant 10 of fa2_bwd_variant enqueues
- * two: dQ, which also computes D, then dK and dV) and allocates nothing: dQ is computed
+ * stream (D, then dK and dV, then dQ) and allocates nothing: dQ is computed
  * by its own kernel over query blocks instead of by atomic adds across key
  * blocks, so results are deterministic.  Validation and error codes as for
  * fa2_fwd (NULL, shape, d, alignment, overlap, argument), before any HIP
@@ -165,45 +207,26 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
                  int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
- * fa2_bwd_variant -- fa2_bwd with an explicit kernel configuration for the
- * dK/dV step, for tuning and for tests that every configuration computes the
- * same gradients.  variant 0 is the default that fa2_bwd uses; the others are
+ * fa2_bwd_variant -- fa2_bwd with an explicit kernel configuration, for
+ * tuning and for tests that every configuration computes the same
+ * gradients.  variant 0 is the default that fa2_bwd uses; the others are
  * described by fa2_bwd_variant_name():
- *   1 "dkdv_w4_occ1": 4 waves x 32 keys per workgroup, one wave per SIMD,
- *     each wave accumulating both dK and dV of its keys;
- *   2 "dkdv_w8_split_occ2": 8 waves, two per SIMD, the two waves of a SIMD
- *     own the same 32 keys, one accumulating dV and the other dK (both
- *     recompute S = Q K^T);
- *   3 "dkdv_w8_split_occ2_ring4": variant 2 with its query tiles copied
- *     straight from memory into a 4-stage LDS ring, three tiles ahead;
- *   4 "dkdv_w8_split_occ2_ring4_dq_ring3", 5 "dkdv_w4_occ1_dq_ring3":
- *     variants 3 and 1 with the dQ kernel's key tiles copied straight from
- *     memory into a 3-stage LDS ring, two tiles ahead (variants 1-3 stage
- *     them through registers, one tile ahead);
- *   6 "dkdv_w8_split_occ2_ring4_q64": variant 3 with 64-query tiles, each
- *     processed as two 32-query sub-blocks between two barriers;
- *   7 "dkdv_w8_pair_occ2_ring3_q64": the dV wave of a SIMD computes S and P
- *     and hands the fp32 P to the dK wave through LDS, so no product is
- *     computed twice; 64-query tiles on a 3-stage copy ring;
- *   8 "dkdv_w8_pair_occ2_ring3_q64_dq_look4": variant 7 with the dQ
- *     kernel's MFMAs issued in a fixed order, 4 operand reads ahead;
- *   9 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4": variant 8 with the
- *     dK/dV kernel's MFMAs ordered the same way;
- *   10 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4_fused_d": variant 9 with
- *     D computed inside the dQ kernel, which then runs first (two kernels
- *     instead of three; delta is written all the same);
- *   11 "dkdv_w4_occ1_dq_w4_look4": variant 1 with 4-wave (128-query) dQ
- *     workgroups at d = 64 (twice the workgroups for small grids); at
- *     d = 128 it is variant 1;
- *   12, 13: variant 9 with 2 and 6 operand reads ahead instead of 4;
- *   14 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4": the P hand-off
- *     pipelined across query tiles, one barrier per iteration (P passed as
- *     16-bit values, dK/dV MFMAs two operand reads ahead).
- *   15 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_pipe_look4": variant 14 with
- *     the dQ kernel pipelined across key tiles too (dQ of tile j-1 from
- *     dS kept in registers, then S, dP, dS of tile j; 4-stage K/V ring).
- * The default is variant 14 for d = 128, variant 1 for non-causal d = 64 and
- * variant 11 for causal d = 64.
+ *   1 "dkdv_w4_occ1": dK/dV workgroups of 4 waves x 32 keys, one wave per
+ *     SIMD, each wave accumulating both dK and dV of its keys; dQ
+ *     workgroups of 8 waves x 32 queries;
+ *   2 "dkdv_w8_pair_occ2_ring3_q64_look4_dq_look4": dK/dV workgroups of 8
+ *     waves, two per SIMD owning the same 32 keys: the dV wave computes S
+ *     and P and hands P to the dK wave through LDS, so no product is
+ *     computed twice; 64-query tiles on a 3-stage copy ring; the MFMAs of
+ *     both kernels issued 4 operand reads ahead;
+ *   3 "dkdv_w4_occ1_dq_w4_look4": variant 1 with 4-wave (128-query) dQ
+ *     workgroups at d = 64, 4 operand reads ahead (twice the workgroups for
+ *     small grids); at d = 128 it is variant 1;
+ *   4 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4": the P hand-off of
+ *     variant 2 pipelined across query tiles, one barrier per iteration,
+ *     dK/dV MFMAs 2 operand reads ahead.
+ * The default is variant 4 for d = 128, variant 1 for non-causal d = 64 and
+ * variant 3 for causal d = 64.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,

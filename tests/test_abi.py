@@ -223,3 +223,58 @@ def test_python_backward_rejects_cpu_tensors(lib):
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError):
         fa2.backward(x, x, x, x, lse, x)
+
+
+# ------------------------------------------------------------ FP8 forward validation
+
+def fchk(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=128, causal=0, scale=0.125, dq=0.01, dk=0.02, dv=0.5):
+    return fa2.lib().fa2_fwd_fp8_check(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv)
+
+
+def test_fp8_valid_arguments_pass(lib):
+    assert fchk() == fa2.FA2_OK
+    assert fchk(d=64, causal=1) == fa2.FA2_OK
+    assert fchk(scale=0.0) == fa2.FA2_OK and fchk(scale=-2.0, dq=-1.0) == fa2.FA2_OK
+    assert fchk(k=Q, v=Q) == fa2.FA2_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa2.FA2_ERR_NULL), (dict(o=None), fa2.FA2_ERR_NULL), (dict(lse=None), fa2.FA2_ERR_NULL),
+    (dict(B=0), fa2.FA2_ERR_SHAPE), (dict(H=-1), fa2.FA2_ERR_SHAPE), (dict(N=0), fa2.FA2_ERR_SHAPE),
+    (dict(N=1 << 24, d=128), fa2.FA2_ERR_SHAPE),                 # one head of o is 4 GiB
+    (dict(d=32), fa2.FA2_ERR_UNSUPPORTED), (dict(d=256), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(v=V + 8), fa2.FA2_ERR_ALIGN), (dict(o=O + 2), fa2.FA2_ERR_ALIGN),
+    (dict(scale=math.nan), fa2.FA2_ERR_ARG), (dict(dq=math.inf), fa2.FA2_ERR_ARG),
+    (dict(dk=math.nan), fa2.FA2_ERR_ARG), (dict(dv=-math.inf), fa2.FA2_ERR_ARG),
+    (dict(scale=1e20, dq=1e20, dk=1e20), fa2.FA2_ERR_ARG),        # c overflows float32
+    (dict(causal=2), fa2.FA2_ERR_ARG),
+    (dict(o=Q), fa2.FA2_ERR_ALIAS), (dict(lse=V + 1024), fa2.FA2_ERR_ALIAS),
+])
+def test_fp8_invalid_arguments(lib, kw, status):
+    assert fchk(**kw) == status
+
+
+def test_fp8_adjacent_buffers_do_not_alias(lib):
+    # inputs are one byte per element, the output two
+    B, H, N, d = 2, 3, 100, 128
+    ib, ob = B * H * N * d, B * H * N * d * 2
+    assert fchk(q=Q, o=Q + ib) == fa2.FA2_OK
+    assert fchk(q=Q, o=Q + ib - 16) == fa2.FA2_ERR_ALIAS
+    assert fchk(o=Q, q=Q + ob) == fa2.FA2_OK
+    assert fchk(o=Q, q=Q + ob - 16) == fa2.FA2_ERR_ALIAS
+
+
+def test_fp8_first_failure_wins(lib):
+    assert fchk(q=None, causal=3) == fa2.FA2_ERR_ARG
+    assert fchk(q=None, N=0) == fa2.FA2_ERR_SHAPE
+    assert fchk(q=None, d=32) == fa2.FA2_ERR_NULL
+    assert fchk(q=Q + 8, d=32) == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_python_fp8_binding_rejects_bad_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fa2.forward_fp8(x, x, x, 1.0, 1.0, 1.0)                  # CPU tensors
+    with pytest.raises(ValueError):
+        fa2.forward_fp8(x.float(), x.float(), x.float(), 1.0, 1.0, 1.0)

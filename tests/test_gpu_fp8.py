@@ -1,0 +1,199 @@
+"""GPU parity of the FP8 forward pass (fa2_fwd_fp8) against the FP8 oracle.
+
+Two kinds of inputs:
+
+* Exact inputs (workloads.make_exact_fp8): every 2^8 P lies on the E4M3 grid,
+  so the tiled model of oracle/fp8.py (tiles of 8192/d keys, reference
+  threshold 0.75 in base 2, P scaled by 2^8) involves no rounding besides the
+  kernel's fp32 accumulation and the bf16 output.  Bound per element:
+      |O - O_model| <= 2^-8 |O_model| + 2^-11 sum_j P~_j |v_j| / l
+  (half an ulp of bf16 is at most 2^-8 |x|; the accumulation term is about 16x
+  the largest error measured for one FP8 MFMA of 64 products, 2^-15 of the
+  sum of their magnitudes), and |LSE - LSE_model| <= 1e-5 + 2^-20 |LSE|.
+* Realistic inputs (workloads.make_inputs_fp8, N(0,1) scaled per tensor):
+  against exact attention of the dequantised inputs, per element
+      |O - O_exact| <= Q + 2^-9 W + 2^-8 |O_exact| + 2^-11 W~
+  with Q = sum_j max(2^-4 P_j, 2^-10) |v_j| / l the rounding of P to E4M3
+  (half the grid spacing), W = sum_j P_j |v_j| / l the effect of the score
+  product's own error on P (relative 2^-10 at most: a relative error e of P
+  moves O by at most 2e W), and the output and accumulation terms above;
+  |LSE - LSE_exact| <= 1e-3.  Because the kernel rounds the same P as the
+  model up to the scores' last bits, its distance to the model is also
+  required to be well below the model's own rounding effect, up to the bf16
+  output rounding:
+      rms(O - O_model) <= 0.25 rms(O_model - O_exact) + 2^-8 rms(O_model).
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_63_amd as fa2
+import workloads as W
+from oracle.fp8 import attention_fp8, attention_online_fp8, dequantise
+from workloads import to_f64
+
+pytestmark = pytest.mark.gpu
+
+LN2 = math.log(2.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    fa2.lib()
+
+
+def tile_keys(d):
+    return 8192 // d
+
+
+def gpu_fp8(q8, k8, v8, desc, causal, scale):
+    o, lse = fa2.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *desc, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    return og, lg
+
+
+def model_head(q8, k8, v8, desc, causal, scale, d):
+    """The tiled model of one head and the weights of its bounds:
+    (O, LSE, sum P~|v|/l, sum P|v|/l, sum max(2^-4 P, 2^-10)|v|/l)."""
+    tiles = []
+    o, lse = attention_online_fp8(q8, k8, v8, *desc, causal, scale, tile_keys(d),
+                                  trace=lambda j0, m, ps, pr: tiles.append((j0, m, ps, pr)))
+    av = np.abs(dequantise(v8, desc[2]))
+    m_f = tiles[-1][1]
+    l = np.zeros(q8.shape[0])
+    wr = np.zeros(q8.shape)
+    wp = np.zeros(q8.shape)
+    qb = np.zeros(q8.shape)
+    for j0, m, ps, pr in tiles:
+        f = np.exp(m - m_f)[:, None]
+        vv = av[j0:j0 + ps.shape[1]]
+        l += (ps * f).sum(axis=1)
+        wr += (pr * f) @ vv
+        wp += (ps * f) @ vv
+        qb += (np.maximum(ps * 2.0 ** -4, 2.0 ** -10) * f) @ vv
+    return o, lse, wr / l[:, None], wp / l[:, None], qb / l[:, None]
+
+
+def heads_of(B, H, heads):
+    return [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+
+
+def check_exact(q8, k8, v8, desc, causal, scale, heads=None, what=""):
+    B, H, N, d = q8.shape
+    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale)
+    worst = 0.0
+    for b, h in heads_of(B, H, heads):
+        args = (q8[b, h].numpy(), k8[b, h].numpy(), v8[b, h].numpy())
+        om, lm, wr, _, _ = model_head(*args, desc, causal, scale, d)
+        err = np.abs(og[b, h] - om)
+        tol = 2.0 ** -8 * np.abs(om) + 2.0 ** -11 * wr
+        worst = max(worst, (err / tol).max())
+        assert (err <= tol).all(), f"{what} head {(b, h)}: max|dO| {err.max():.3e}, worst ratio {(err / tol).max():.2f}"
+        el = np.abs(lg[b, h] - lm)
+        assert (el <= 1e-5 + 2.0 ** -20 * np.abs(lm)).all(), f"{what} head {(b, h)}: max|dLSE| {el.max():.3e}"
+    print(f"{what}: worst error / bound {worst:.3f}", flush=True)
+
+
+def check_real(q8, k8, v8, desc, causal, scale, heads=None, what=""):
+    B, H, N, d = q8.shape
+    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale)
+    d_km, d_mx, o_m = [], [], []
+    for b, h in heads_of(B, H, heads):
+        args = (q8[b, h].numpy(), k8[b, h].numpy(), v8[b, h].numpy())
+        om, lm, wr, wp, qb = model_head(*args, desc, causal, scale, d)
+        ox, lx = attention_fp8(*args, *desc, causal, scale)
+        err = np.abs(og[b, h] - ox)
+        tol = qb + 2.0 ** -9 * wp + 2.0 ** -8 * np.abs(ox) + 2.0 ** -11 * wr
+        assert (err <= tol).all(), f"{what} head {(b, h)}: max|dO| {err.max():.3e} over the bound"
+        assert np.abs(lg[b, h] - lx).max() <= 1e-3, f"{what} head {(b, h)}: LSE"
+        d_km.append((og[b, h] - om).ravel())
+        d_mx.append((om - ox).ravel())
+        o_m.append(om.ravel())
+    rms = lambda x: np.sqrt(np.mean(np.concatenate(x) ** 2))
+    rms_km, rms_mx, rms_o = rms(d_km), rms(d_mx), rms(o_m)
+    print(f"{what}: rms(kernel - model) {rms_km:.3e}, rms(model - exact) {rms_mx:.3e}, rms(O) {rms_o:.3e}",
+          flush=True)
+    assert rms_km <= 0.25 * rms_mx + 2.0 ** -8 * rms_o, f"{what}: kernel strays from the model"
+
+
+EXACT_CASES = [
+    (1, 2, 300, 128, False), (1, 2, 300, 128, True), (2, 1, 517, 64, False), (1, 3, 517, 64, True),
+    (1, 1, 1, 128, False), (1, 1, 1, 64, True), (1, 1, 64, 128, True), (1, 1, 65, 128, False),
+    (1, 2, 1000, 128, True), (1, 1, 257, 64, False), (1, 1, 129, 64, True), (3, 3, 256, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", EXACT_CASES)
+def test_fp8_exact_inputs(B, H, N, d, causal):
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(B, H, N, d, seed=N + d)
+    check_exact(q8, k8, v8, desc, causal, scale, what=f"exact B{B} H{H} N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("scale_factor", [-1.0, 0.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_exact_inputs_scale_sign(scale_factor, d):
+    # a negative scale flips the sign of Q inside the kernel; scale 0 gives
+    # uniform weights: both stay exact on these inputs
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(1, 2, 333, d, seed=7)
+    check_exact(q8, k8, v8, desc, True, scale * scale_factor, what=f"scale x{scale_factor} d{d}")
+
+
+REAL_CASES = [(1, 2, 700, 128, False), (1, 2, 700, 128, True), (1, 2, 700, 64, False), (1, 2, 700, 64, True),
+              (1, 1, 1, 128, False), (2, 1, 77, 64, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", REAL_CASES)
+def test_fp8_realistic_inputs(B, H, N, d, causal):
+    (q8, k8, v8), desc = W.make_inputs_fp8(B, H, N, d, seed=N + 3 * d)
+    check_real(q8, k8, v8, desc, causal, 1 / math.sqrt(d), what=f"real B{B} H{H} N{N} d{d} causal={causal}")
+
+
+def test_fp8_realistic_inputs_key_offset():
+    # per-key-row offsets on K (the long causal workload's recipe): the
+    # reference moves often and P spans many binades
+    (q8, k8, v8), desc = W.make_inputs_fp8(1, 2, 1024, 128, seed=5, sigma=0.5, key_offset=(-4.0, 4.0))
+    check_real(q8, k8, v8, desc, True, 1 / math.sqrt(128), what="key offset")
+
+
+@pytest.mark.parametrize("name", sorted(W.FP8_WORKLOADS))
+def test_fp8_workloads(name):
+    w = W.FP8_WORKLOADS[name]
+    (q8, k8, v8), desc = W.workload_inputs_fp8(w)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
+    check_real(q8, k8, v8, desc, w.causal, w.scale, heads=heads, what=name)
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(w.B, w.H, w.N, w.d, seed=w.seed)
+    check_exact(q8, k8, v8, desc, w.causal, scale, heads=heads, what=name + " exact inputs")
+
+
+def test_fp8_deterministic_and_c_abi():
+    (q8, k8, v8), desc = W.make_inputs_fp8(2, 2, 300, 128, seed=12)
+    q, k, v = q8.cuda(), k8.cuda(), v8.cuda()
+    o1, l1 = fa2.forward_fp8(q, k, v, *desc, causal=True)
+    o2, l2 = fa2.forward_fp8(q, k, v, *desc, causal=True)
+    o3 = torch.empty_like(o1)
+    l3 = torch.empty_like(l1)
+    rc = fa2.lib().fa2_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o3.data_ptr(), l3.data_ptr(),
+                               2, 2, 300, 128, 1, ctypes.c_float(1 / math.sqrt(128)), *desc,
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == fa2.FA2_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_fp8_invalid_call_writes_nothing():
+    (q8, k8, v8), desc = W.make_inputs_fp8(1, 1, 64, 128, seed=1)
+    q, k, v = q8.cuda(), k8.cuda(), v8.cuda()
+    o = torch.full((1, 1, 64, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((1, 1, 64), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(fa2.Fa2Error):
+        fa2.forward_fp8(q, k, v, math.inf, 1.0, 1.0, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert (o == 7.0).all() and (lse == 7.0).all()
