@@ -10,6 +10,8 @@ scale 1/sqrt(d), inputs resident in HBM.  Prints ONE JSON line on stdout.
 
 Throughput is counted as 4*B*H*N^2*d FLOPs per call (halved when causal).
 Timing uses HIP events recorded on the stream the kernel is launched on.
+The FP8 workloads (--workload b8h32n2048d128_fp8, ...) time fa2_fwd_fp8 on
+E4M3 inputs with a bf16 output, against the dense FP8 MFMA peak.
 
 --backward times the backward pass instead (one step = one fa2_bwd call:
 the D, dK/dV and dQ kernels on one stream), counted as 10*B*H*N^2*d FLOPs
@@ -30,11 +32,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS (and % of MFMA peak) at N=2048,d=128 bf16"
+FP8_METRIC = "attention fwd TFLOPS (and % of FP8 MFMA peak), E4M3 inputs, 4*B*H*N^2*d FLOPs per call"
 BWD_METRIC = "attention bwd TFLOPS (and % of MFMA peak), 10*B*H*N^2*d FLOPs per call"
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}   # MI355X dense MFMA peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
+# MI355X dense MFMA peaks: 256 CU x 2.4 GHz x 4096 FLOP/clk (16-bit), x 8192 (FP8)
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "exact_attention_63_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_sched.hpp", "fa2_fwd_sched.inc")]
+FP8_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_fp8.hpp")]
 PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
 
 
@@ -43,8 +48,14 @@ def kernel_identity(w, variant: int = 0) -> str:
     workload runs with: the counters recorded for one identity are only reused
     for exactly that kernel."""
     import exact_attention_63_amd as fa2
-    vi = variant or fa2.default_variant(0 if w.dtype == "fp16" else 1, w.d, w.causal)
     h = hashlib.sha256()
+    if w.dtype == "fp8":
+        for src in FP8_KERNEL_SOURCES:
+            with open(src, "rb") as f:
+                h.update(f.read())
+        h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
+        return h.hexdigest()[:16]
+    vi = variant or fa2.default_variant(0 if w.dtype == "fp16" else 1, w.d, w.causal)
     for src in KERNEL_SOURCES:
         with open(src, "rb") as f:
             h.update(f.read())
@@ -121,24 +132,26 @@ def host_info():
     return cores, blas, model
 
 
-def mfma_probe(iters: int = 100000):
-    """Sustained dense bf16 MFMA throughput (TFLOP/s) and shader clock (GHz)
-    measured now by bench_probe.so (an MFMA-only loop on every CU), or None
-    when the probe is not built."""
+def mfma_probe(iters: int = 100000, fp8: bool = False):
+    """Sustained dense bf16 (or FP8) MFMA throughput (TFLOP/s) and shader clock
+    (GHz) measured now by bench_probe.so (an MFMA-only loop on every CU), or
+    None when the probe is not built."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         return None
     import torch
     lib = ctypes.CDLL(PROBE_LIB)
-    lib.fa2_probe_mfma.restype = ctypes.c_int
-    lib.fa2_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
-                                   ctypes.POINTER(ctypes.c_double)]
+    fn = lib.fa2_probe_mfma_fp8 if fp8 else lib.fa2_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     tf, ghz = ctypes.c_double(), ctypes.c_double()
-    rc = lib.fa2_probe_mfma(iters, torch.cuda.current_stream().cuda_stream, ctypes.byref(tf), ctypes.byref(ghz))
+    rc = fn(iters // 4 if fp8 else iters, torch.cuda.current_stream().cuda_stream, ctypes.byref(tf),
+            ctypes.byref(ghz))
     if rc != 0:
-        raise RuntimeError(f"fa2_probe_mfma failed with HIP error {rc}")
+        raise RuntimeError(f"MFMA probe failed with HIP error {rc}")
+    inst = "v_mfma_f32_32x32x64_f8f6f4 (E4M3)" if fp8 else "v_mfma_f32_32x32x16_bf16"
     return {"value": round(tf.value, 1), "unit": "TFLOP/s", "clock_ghz": round(ghz.value, 3),
-            "what": "bench_probe.hip: back-to-back v_mfma_f32_32x32x16_bf16, 2 waves per SIMD on every CU, "
+            "what": f"bench_probe.hip: back-to-back {inst}, 2 waves per SIMD on every CU, "
                     "random operands, run right after the timed region"}
 
 
@@ -146,16 +159,26 @@ def cpu_baseline(w, budget_s: float = 20.0):
     """The fp64 CPU oracle timed on whole heads of the same workload (in order)
     until about budget_s seconds of work are done or every head is done."""
     import oracle
-    from workloads import workload_inputs, to_f64
+    from workloads import workload_inputs, workload_inputs_fp8, to_f64
     host_cores, blas, model = host_info()
     cores = min(blas, host_cores)
-    q, k, v = workload_inputs(w)
+    if w.dtype == "fp8":
+        (q8, k8, v8), desc = workload_inputs_fp8(w)
+
+        def one_head(b, h):
+            oracle.attention_fp8(q8[b, h].numpy(), k8[b, h].numpy(), v8[b, h].numpy(), *desc, w.causal, w.scale)
+        what = "fp64 NumPy oracle (E4M3 decoding, then the 3-pass definition)"
+    else:
+        q, k, v = workload_inputs(w)
+
+        def one_head(b, h):
+            oracle.attention_3pass(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.causal, w.scale)
+        what = "fp64 NumPy 3-pass oracle"
     nh = w.B * w.H
     heads = 0
     t0 = time.perf_counter()
     while heads < nh:
-        b, h = divmod(heads, w.H)
-        oracle.attention_3pass(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.causal, w.scale)
+        one_head(*divmod(heads, w.H))
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -163,8 +186,8 @@ def cpu_baseline(w, budget_s: float = 20.0):
     flops_per_head = w.flops / nh
     return {"value": round(heads * flops_per_head / dt / 1e12, 6), "unit": "TFLOPS", "cores": cores,
             "host_cores": host_cores, "blas_threads": blas, "cpu_model": model, "kind": "oracle",
-            "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, fp64 NumPy "
-                      f"3-pass oracle, {dt:.1f} s; TFLOPS counted like the GPU figure"}
+            "sample": f"{heads} of {nh} heads (all {w.N} rows each) of {w.name}, {what}, "
+                      f"{dt:.1f} s; TFLOPS counted like the GPU figure"}
 
 
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_63_amd", "csrc", "fa2_bwd_kernel.hpp")
@@ -296,13 +319,21 @@ def backward_main(args, w):
 def run_workload(w, steps, warmup, variant=0):
     import torch
     import exact_attention_63_amd as fa2
-    from workloads import workload_inputs
-    q, k, v = (t.cuda() for t in workload_inputs(w))
-    o = torch.empty_like(q)
+    from workloads import workload_inputs, workload_inputs_fp8
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    if w.dtype == "fp8":
+        (q8, k8, v8), desc = workload_inputs_fp8(w)
+        q, k, v = (t.cuda() for t in (q8, k8, v8))
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
 
-    def step():
-        fa2.forward(q, k, v, causal=w.causal, scale=w.scale, variant=variant, out=o, lse=lse)
+        def step():
+            fa2.forward_fp8(q, k, v, *desc, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    else:
+        q, k, v = (t.cuda() for t in workload_inputs(w))
+        o = torch.empty_like(q)
+
+        def step():
+            fa2.forward(q, k, v, causal=w.causal, scale=w.scale, variant=variant, out=o, lse=lse)
 
     ms, wall_ms = time_gpu(step, steps, warmup)
     run_workload.last_stats = per_call_stats(step, steps)
@@ -348,9 +379,15 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
 
-    from workloads import HEADLINE, WORKLOADS
+    from workloads import FP8_WORKLOADS, HEADLINE, WORKLOADS
     name = args.workload or HEADLINE
-    w = WORKLOADS[name]
+    if name not in WORKLOADS and name not in FP8_WORKLOADS:
+        print(f"unknown workload {name}; choose from {sorted(WORKLOADS) + sorted(FP8_WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS.get(name) or FP8_WORKLOADS[name]
+    if args.backward and w.dtype == "fp8":
+        print("the backward pass takes fp16 or bf16 inputs", file=sys.stderr)
+        sys.exit(2)
     if args.backward:
         backward_main(args, w)
         return
@@ -362,14 +399,15 @@ def main():
 
     if args.all:
         print(f"{'workload':36s} {'ms':>9s} {'TFLOPS':>9s} {'%peak':>7s}", file=sys.stderr)
-        for other in WORKLOADS.values():
+        for other in list(WORKLOADS.values()) + list(FP8_WORKLOADS.values()):
             oms, _ = run_workload(other, max(5, args.steps // 2), max(2, args.warmup // 2), args.variant)
             t = other.flops / (oms * 1e-3) / 1e12
             print(f"{other.name:36s} {oms:9.4f} {t:9.1f} {100 * t / PEAK_TFLOPS[other.dtype]:6.1f}%",
                   file=sys.stderr, flush=True)
 
+    fp8 = w.dtype == "fp8"
     line = {
-        "metric": METRIC,
+        "metric": FP8_METRIC if fp8 else METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -379,8 +417,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs, rounded to the dtype)",
+        "dtype": "fp8_e4m3" if fp8 else w.dtype,
+        "data": ("synthetic (seeded N(0,1) inputs as E4M3 codes with one descale per tensor, bf16 output)" if fp8
+                 else "synthetic (seeded N(0,1) inputs, rounded to the dtype)"),
         "config": {**w.describe(), "variant": args.variant, "parallelism": "single GPU",
                    "wall_ms_per_step": round(wall_ms, 5), "per_call": stats},
         "roofline": {
@@ -392,7 +431,7 @@ def main():
             "traffic": traffic,
         },
     }
-    probe = mfma_probe()
+    probe = mfma_probe(fp8=fp8)
     if probe is not None:
         line["roofline"]["probe_peak"] = probe
         line["roofline"]["frac_probe"] = round(tflops / probe["value"], 4)

@@ -209,8 +209,13 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
 // ---- FP8 forward ------------------------------------------------------------
 
 typedef void (*fp8_fn)(fa2::Fp8Args);
-const fp8_fn kFp8[2][2] = {{fa2::fa2_fwd_fp8_kernel<64, false>, fa2::fa2_fwd_fp8_kernel<64, true>},
-                           {fa2::fa2_fwd_fp8_kernel<128, false>, fa2::fa2_fwd_fp8_kernel<128, true>}};
+// 4-wave workgroups, three per CU: measured on MI355X against 8-wave
+// workgroups (two waves per SIMD of one workgroup), bitwise-equal results:
+// 0.348 against 0.408 ms on B=8, H=32, N=2048, d=128; 0.116 against 0.122 ms
+// on B=2, H=16, N=4096, d=128, causal; 20.3 against 21.3 us at d = 64.
+constexpr int kW = fa2::kFp8Waves, kOcc = fa2::kFp8Occupancy;
+const fp8_fn kFp8[2][2] = {{fa2::fa2_fwd_fp8_kernel<64, false, kW, kOcc>, fa2::fa2_fwd_fp8_kernel<64, true, kW, kOcc>},
+                           {fa2::fa2_fwd_fp8_kernel<128, false, kW, kOcc>, fa2::fa2_fwd_fp8_kernel<128, true, kW, kOcc>}};
 
 // c = scale * descale_q * descale_k * log2(e), in double, then float
 float fp8_exponent_scale(float scale, float dq, float dk) {
@@ -260,7 +265,7 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.c = fp8_exponent_scale(scale, dq, dk);
   a.dv = dv;
   const uint64_t blocks = (uint64_t)a.nqb * bh;
-  hipLaunchKernelGGL(kFp8[d == 128][causal], dim3((unsigned)blocks), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(kFp8[d == 128][causal], dim3((unsigned)blocks), dim3(64 * kW), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }

@@ -16,15 +16,17 @@
 //   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation; the unit
 //     E8M0 scale 0x7f leaves the products unscaled).
 //   * The reference max of a row moves only when a tile's max exceeds it by
-//     more than kFp8Lazy = 0.75 (base 2): the conditional rescale of the v4
-//     diagram in its exact form.  P = 2^(c s - m + 8) then never exceeds
-//     2^8.75 < 448, and its small values stay out of the E4M3 subnormals down
-//     to 2^-14 of the row max.  P is rounded to E4M3 (nearest even,
-//     v_cvt_pk_fp8_f32) for O^T += V^T P^T on the same FP8 MFMA; the row sum
-//     l takes the fp32 P.  O = acc * (dv / l), LSE = (m + log2 l - 8) ln 2.
+//     more than kFp8Lazy = 2.75 (base 2): the conditional rescale of the v4
+//     diagram in its exact form.  P = 2^(c s - m + 6) then never exceeds
+//     2^8.75 < 448, and its values down to 2^-12 of the reference stay normal
+//     E4M3 numbers; a group of 32 rows rescales acc in about 6 % of the
+//     tiles of N(0,1) inputs (about half with a shift of 8 and a threshold of
+//     0.75).  P is rounded to E4M3 (nearest even, v_cvt_pk_fp8_f32) for
+//     O^T += V^T P^T on the same FP8 MFMA; the row sum l takes the fp32 P.
+//     O = acc * (dv / l), LSE = (m + log2 l - 6) ln 2.
 //
 // Layout (d = 128: 64-key tiles; d = 64: 128-key tiles; one tile of K or V is
-// 8 KiB either way, so each of the 8 waves copies 1 KiB of each):
+// 8 KiB either way, copied in 1 KiB blocks by the waves of the workgroup):
 //   * A K tile is [key][d] bytes.  The score MFMA's A operand is 32 bytes of
 //     one key row per lane (d in [64s + 32h, +32) for lane half h of d step
 //     s), its B operand the same bytes of the lane's query row, held in
@@ -67,10 +69,12 @@ struct Fp8Args {
   float dv;    // descale of V
 };
 
-constexpr int kFp8Rows = 256;        // query rows per workgroup (8 waves x 32)
 constexpr int kFp8TileBytes = 8192;  // one K (or V) tile: 8192 / d keys
-constexpr float kFp8Lazy = 0.75f;    // reference threshold, base 2
-constexpr float kFp8Shift = 8.f;     // P is scaled by 2^8 before rounding to E4M3
+constexpr float kFp8Lazy = 2.75f;    // reference threshold, base 2
+constexpr float kFp8Shift = 6.f;     // P is scaled by 2^6 before rounding to E4M3
+constexpr int kFp8Waves = 4;         // waves per workgroup of the launched kernel
+constexpr int kFp8Rows = 32 * kFp8Waves;   // its query rows per workgroup
+constexpr int kFp8Occupancy = 3;     // its waves per SIMD: three workgroups per CU
 
 // XOR swizzle of the 16-byte chunks of a [key][d] row of d bytes (d = 128: 8
 // chunks, d = 64: 4 chunks).  d = 128: bits 1, 3, 2 of the row give bits 1, 2,
@@ -118,137 +122,143 @@ __device__ __forceinline__ void use_vgprs(const i32x8& x) { asm volatile("" ::"v
 
 // four fp32 -> four E4M3 bytes in order (round to nearest even)
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the first conversion's other half is overwritten by the second one
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
 
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void fa2_fwd_fp8_kernel(Fp8Args a) {
-  constexpr int TSZ = kFp8TileBytes;
-  constexpr int BR = kFp8Rows;
-  constexpr int BC = TSZ / D;        // keys per tile
-  constexpr int KB = BC / 32;        // 32-key blocks per tile
-  constexpr int KS = D / 64;         // 64-wide d steps of the score product
-  constexpr int DB = D / 32;         // 32-row blocks of O^T
-  constexpr int PS = BC / 64;        // 64-key steps of the P.V product
-  constexpr int NS = 3;              // ring stages
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+template <int D, int NW>
+struct Fp8Geom {
+  static constexpr int TSZ = kFp8TileBytes;
+  static constexpr int BR = NW * 32;   // query rows per workgroup (NW waves x 32)
+  static constexpr int CPW = 8 / NW;   // 1 KiB copy blocks per wave, tile and tensor
+  static constexpr int BC = TSZ / D;   // keys per tile
+  static constexpr int KB = BC / 32;   // 32-key blocks per tile
+  static constexpr int KS = D / 64;    // 64-wide d steps of the score product
+  static constexpr int DB = D / 32;    // 32-row blocks of O^T
+  static constexpr int PS = BC / 64;   // 64-key steps of the P.V product
+};
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int lr = lane & 31;
-  const int lh = lane >> 5;
+// One wave's view of a workgroup: its head, rows, Q fragments, online-softmax
+// state and fragment addresses.  The kernels below differ only in how they
+// order the steps of the loop over key tiles.
+template <int D, bool CAUSAL, int NW>
+struct Fp8Wave {
+  using G = Fp8Geom<D, NW>;
+  __amdgpu_buffer_rsrc_t kr, vr;
+  int bh, N, q_wg, q_w, nt, lr, lh;
+  float c;                 // |scale * dq * dk * log2(e)|
+  i32x8 qf[G::KS];         // B operand of S^T = K Q^T
+  f32x16 acc[G::DB];       // O^T
+  float m_run, l_run;      // reference max and row sum (base 2, P scaled by 2^6)
+  uint32_t dsrc[G::CPW];   // copy source offsets in a tile
+  uint32_t ldsw;           // this wave's LDS destination in a stage
+  int ka[2], vb;           // K and V^T fragment addresses inside a stage
 
-  // ---- workgroup -> (query block, head), as the 16-bit kernels ------------
-  int bh, qblk;
-  {
-    const int i = blockIdx.x;
-    const int total = a.nqb * a.BH;
-    if constexpr (!CAUSAL) {
-      const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
-      bh = logical / a.nqb;
-      qblk = logical % a.nqb;
-    } else {
-      causal_item(i, a.BH, a.nqb, bh, qblk);
+  __device__ __forceinline__ void init(const Fp8Args& a, uint8_t* smem) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    lr = lane & 31;
+    lh = lane >> 5;
+    int qblk;
+    {
+      const int i = blockIdx.x;
+      const int total = a.nqb * a.BH;
+      if constexpr (!CAUSAL) {
+        const int logical = (total % 8 == 0) ? (i % 8) * (total / 8) + i / 8 : i;
+        bh = logical / a.nqb;
+        qblk = logical % a.nqb;
+      } else {
+        causal_item(i, a.BH, a.nqb, bh, qblk);
+      }
     }
-  }
-  const int N = a.N;
-  const size_t head_off = (size_t)bh * (size_t)N * D;   // elements (= bytes of the inputs)
-  const uint32_t head_bytes = (uint32_t)N * D;
-  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.q + head_off), 0, head_bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.k + head_off), 0, head_bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.v + head_off), 0, head_bytes, kBufferWord3);
+    N = a.N;
+    const size_t head_off = (size_t)bh * (size_t)N * D;   // elements = bytes of the inputs
+    const uint32_t head_bytes = (uint32_t)N * D;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)a.q + head_off), 0, head_bytes, kBufferWord3);
+    kr = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.k + head_off), 0, head_bytes, kBufferWord3);
+    vr = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.v + head_off), 0, head_bytes, kBufferWord3);
+    q_wg = qblk * G::BR;
+    q_w = q_wg + wave * 32;
+    nt = (N + G::BC - 1) / G::BC;
+    if constexpr (CAUSAL) nt = min(nt, (min(q_wg + G::BR, N) - 1) / G::BC + 1);
 
-  const int q_wg = qblk * BR;
-  const int q_w = q_wg + wave * 32;          // first query row of this wave
-  int nt = (N + BC - 1) / BC;
-  if constexpr (CAUSAL) {
-    const int last_row = min(q_wg + BR, N) - 1;
-    nt = min(nt, last_row / BC + 1);
-  }
-
-  // ---- Q fragments: B operand of S^T = K Q^T, kept in VGPRs --------------
-  i32x8 qf[KS];
-  {
+    // Q: bytes [64 s + 32 lh, +32) of query row q_w + lr
     const uint32_t qoff = (uint32_t)((q_w + lr) * D + 32 * lh);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < G::KS; ++s) {
       const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 64 * s, 0, 0);
       const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 64 * s + 16, 0, 0);
       qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
+    // a negative c flips the sign bit of every Q code (exact), so c >= 0 below
+    c = a.c;
+    if (c < 0.f) {
+      c = -c;
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s) qf[s] ^= (int)0x80808080u;
+    }
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) acc[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    // copies: wave w moves bytes [1024 CPW w, 1024 CPW (w + 1)) of each tile
+#pragma unroll
+    for (int k = 0; k < G::CPW; ++k) {
+      const int b = (wave * G::CPW + k) * 1024 + 16 * lane;
+      const int row = b / D, phys = (b % D) / 16;
+      dsrc[k] = (uint32_t)(row * D + 16 * (phys ^ fp8_swizzle<D>(row)));
+    }
+    ldsw = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem +
+                                          (uint32_t)(wave * G::CPW) * 1024u);
+    // K: row 32 kb + lr, chunks 4 s + 2 lh + e (e = 0, 1)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) ka[e] = lr * D + 16 * ((2 * lh + e) ^ fp8_swizzle<D>(lr));
+    // V^T: lane j = lane % 16 of group g = lane / 16 reads row
+    // 64 u + 16 x + 8 (r / 4) + 4 h + r % 4 (r = j / 2, h = g / 2) at column
+    // 32 db + 16 (g % 2) + 8 (j % 2); the swizzle depends on r and h only
+    {
+      const int g = lane >> 4, j = lane & 15, r = j >> 1;
+      const int vrow = 8 * (r >> 2) + 4 * (g >> 1) + (r & 3);
+      vb = vrow * D + 16 * ((g & 1) ^ fp8_swizzle<D>(vrow)) + 8 * (j & 1);
+    }
   }
 
-  // ---- per-row state (base 2) --------------------------------------------
-  f32x16 acc[DB];
+  // this wave's share of one tile's K (or V) copy into the LDS stage at byte
+  // offset stage_off: CPW instructions
+  __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, int tile, uint32_t stage_off) const {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  // A negative c flips the sign bit of every Q code (exact), so c >= 0 below.
-  const bool c_neg = a.c < 0.f;
-  const float c = c_neg ? -a.c : a.c;
-  if (c_neg) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] ^= (int)0x80808080u;
+    for (int k = 0; k < G::CPW; ++k) lds_copy16(r, ldsw + stage_off + 1024 * k, dsrc[k] + (uint32_t)tile * G::TSZ);
   }
 
-  // ---- copies: wave w moves bytes [1024 w, 1024 w + 1024) of each tile -----
-  uint32_t dsrc;
-  {
-    const int b = wave * 1024 + 16 * lane;
-    const int row = b / D, phys = (b % D) / 16;
-    dsrc = (uint32_t)(row * D + 16 * (phys ^ fp8_swizzle<D>(row)));
-  }
-  // LDS byte address of this wave's 1 KiB of stage 0 (wave-uniform)
-  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + (uint32_t)wave * 1024u);
-  auto dma = [&](int tile, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    const uint32_t off = dsrc + (uint32_t)tile * TSZ;
-    lds_copy16(kr, ldsw + S * TSZ, off);
-    lds_copy16(vr, ldsw + (NS + S) * TSZ, off);
-  };
-
-  // ---- fragment addresses ---------------------------------------------------
-  // K: row 32 kb + lr, chunks 4 s + 2 lh + e (e = 0, 1)
-  int ka[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) ka[e] = lr * D + 16 * ((2 * lh + e) ^ fp8_swizzle<D>(lr));
-  // V^T: lane j = lane % 16 of group g = lane / 16 reads row
-  // 64 u + 16 x + 8 (r / 4) + 4 h + r % 4 (r = j / 2, h = g / 2) at column
-  // 32 db + 16 (g % 2) + 8 (j % 2); the swizzle depends on r and h only
-  int vb;
-  {
-    const int g = lane >> 4, j = lane & 15, r = j >> 1;
-    const int vrow = 8 * (r >> 2) + 4 * (g >> 1) + (r & 3);
-    vb = vrow * D + 16 * ((g & 1) ^ fp8_swizzle<D>(vrow)) + 8 * (j & 1);
+  __device__ __forceinline__ bool masked(int key0) const {
+    return (key0 + G::BC > N) || (CAUSAL && key0 + G::BC - 1 > q_w);
   }
 
-  auto tile_skip = [&](int key0) { return CAUSAL && key0 > q_w + 31; };
-  auto tile_masked = [&](int key0) { return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w); };
+  // one 32-key block of S^T = K Q^T from the K tile at ks
+  __device__ __forceinline__ void score_block(const uint8_t* ks, int kb, f32x16& sb) const {
+    sb = f32x16{};
+#pragma unroll
+    for (int s = 0; s < G::KS; ++s) {
+      const uint8_t* kp = ks + 32 * kb * D;
+      const u32x4 lo = *(const u32x4*)(kp + (ka[0] ^ (64 * s)));
+      const u32x4 hi = *(const u32x4*)(kp + (ka[1] ^ (64 * s)));
+      const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sb = mfma_fp8(kf, qf[s], sb);
+    }
+  }
 
-  // ---- one key tile: scores, softmax, P.V -----------------------------------
-  auto tile = [&](int j, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    const int key0 = j * BC;
-    if (tile_skip(key0)) return;
-    const uint8_t* ks = smem + S * TSZ;
-    const uint8_t* vs = smem + (NS + S) * TSZ;
-
-    // S^T = K Q^T
-    f32x16 sc[KB];
+  // S^T = K Q^T from the K tile at ks
+  __device__ __forceinline__ void scores(const uint8_t* ks, f32x16 (&sc)[G::KB]) const {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{};
+    for (int kb = 0; kb < G::KB; ++kb) sc[kb] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < G::KS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < G::KB; ++kb) {
         const uint8_t* kp = ks + 32 * kb * D;
         const u32x4 lo = *(const u32x4*)(kp + (ka[0] ^ (64 * s)));
         const u32x4 hi = *(const u32x4*)(kp + (ka[1] ^ (64 * s)));
@@ -257,19 +267,24 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
         sc[kb] = mfma_fp8(kf, qf[s], sc[kb]);
       }
     }
-    // keep the phases apart: hoisting the P.V operand reads above the softmax
-    // would hold them in registers beside the scores
-    __builtin_amdgcn_sched_barrier(0);
+  }
 
-    // tile max (base 2)
-    float cc = c, m_tile;
-    if (tile_masked(key0)) {
-      // key key0 + 4 lh + off (off = 32 kb + 8 (r / 4) + r % 4) is visible iff
-      // off < lim: one per-lane bound against compile-time offsets
+  // online softmax of one tile of scores (keys from key0), in two parts.
+  // ref_update: masks the scores (MASKED), takes the tile max, moves the
+  // reference when the max exceeds it by more than kFp8Lazy, and returns
+  // alpha = 2^(m_old - m_new), the multiplier cc of the stored scores and
+  // the subtrahend ref of the exponent (P is scaled by 2^6).
+  template <bool MASKED>
+  __device__ __forceinline__ void ref_update(f32x16 (&sc)[G::KB], int key0, float& alpha, float& cc, float& ref) {
+    float m_tile;
+    cc = c;
+    if constexpr (MASKED) {
+      // key key0 + 4 lh + off (off = 32 kb + 8 (r / 4) + r % 4) is visible
+      // iff off < lim: one per-lane bound against compile-time offsets
       const int lim = (CAUSAL ? min(N, q_w + lr + 1) : N) - key0 - 4 * lh;
       float e0 = -INFINITY, e1 = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const bool vis = 32 * kb + 8 * (r >> 2) + (r & 3) < lim;
@@ -282,7 +297,7 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
     } else {
       float e0 = sc[0][0], e1 = sc[0][1];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
           e0 = fmaxf(e0, fmaxf(sc[kb][r], sc[kb][r + 1]));
@@ -293,38 +308,49 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
     const float m_old = m_run;
     const float m_new = (m_tile > m_old + kFp8Lazy) ? m_tile : m_old;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+    alpha = __builtin_amdgcn_exp2f(m_old - m_use);
     m_run = m_new;
-    const float ref = m_use - kFp8Shift;
-
-    // P = 2^(c s - ref), row sum over fp32 P, E4M3 for the product
-    i32x8 pk[PS];
-    float rs0 = 0.f, rs1 = 0.f;
+    ref = m_use - kFp8Shift;
+  }
+  // exp_block: P = 2^(cc s - ref) of one 32-key block, added to the row sums
+  // (fp32) and packed as E4M3 in the B-operand order of the P.V product
+  __device__ __forceinline__ void exp_block(const f32x16& s, int kb, float cc, float ref, i32x8 (&pk)[G::PS],
+                                            float& rs0, float& rs1) const {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int w = 0; w < 4; ++w) {
+      float p[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float p[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w + t], cc, -ref));
-          if (t & 1) rs1 += p[t]; else rs0 += p[t];
-        }
-        pk[kb >> 1][4 * (kb & 1) + w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);
+      for (int t = 0; t < 4; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * w + t], cc, -ref));
+        if (t & 1) rs1 += p[t]; else rs0 += p[t];
       }
+      pk[kb >> 1][4 * (kb & 1) + w] = (int)pack_fp8x4(p[0], p[1], p[2], p[3]);
     }
+  }
+  // both parts over the whole tile
+  template <bool MASKED>
+  __device__ __forceinline__ void softmax(f32x16 (&sc)[G::KB], int key0, i32x8 (&pk)[G::PS], float& alpha) {
+    float cc, ref, rs0 = 0.f, rs1 = 0.f;
+    ref_update<MASKED>(sc, key0, alpha, cc, ref);
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb) exp_block(sc[kb], kb, cc, ref, pk, rs0, rs1);
     l_run = l_run * alpha + (rs0 + rs1);
+  }
+
+  // acc *= alpha when some row of the wave moved its reference
+  __device__ __forceinline__ void rescale(float alpha) {
     if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
     }
+  }
 
-    __builtin_amdgcn_sched_barrier(0);
-    // O^T += V^T P^T
+  // O^T += V^T P^T from the V tile at vs
+  __device__ __forceinline__ void pv(const uint8_t* vs, const i32x8 (&pk)[G::PS]) {
 #pragma unroll
-    for (int u = 0; u < PS; ++u) {
+    for (int u = 0; u < G::PS; ++u) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < G::DB; ++db) {
         i32x8 vf;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -335,33 +361,102 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
         acc[db] = mfma_fp8(vf, pk[u], acc[db]);
       }
     }
+  }
+
+  // O = acc * (dv / l) in bf16, LSE = (m + log2 l - 6) ln 2
+  __device__ __forceinline__ void store(const Fp8Args& a) const {
+    const size_t head_off = (size_t)bh * (size_t)N * D;
+    const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((uint16_t*)a.o + head_off), 0, (uint32_t)N * D * 2u, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t lsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
+    const int row = q_w + lr;
+    const float l = sum_halves(l_run);
+    const float so = a.dv / l;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = Elem<true>::pack(acc[db][4 * i + 0] * so, acc[db][4 * i + 1] * so);
+        w[1] = Elem<true>::pack(acc[db][4 * i + 2] * so, acc[db][4 * i + 3] * so);
+        const int d = 32 * db + 8 * i + 4 * lh;
+        __builtin_amdgcn_raw_buffer_store_b64(w, orr, (uint32_t)(row * D * 2 + d * 2), 0, 0);
+      }
+    }
+    if (lh == 0) {
+      const float lse = (m_run + log2f(l) - kFp8Shift) * 0.69314718055994530942f;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lsr, (uint32_t)(row * 4), 0, 0);
+    }
+  }
+};
+
+// Tile by tile: S, softmax and P.V of tile j between two barriers, the copy
+// of tile j + 2 in flight meanwhile (3-stage ring of K and V tiles).  NW
+// waves per workgroup: with 4, two workgroups share a CU and their barriers
+// are independent, so one's softmax overlaps the other's matrix products.
+// WPE: waves per SIMD the register budget is sized for (3: at most 168
+// VGPRs, three 4-wave workgroups per CU).
+template <int D, bool CAUSAL, int NW, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+void fa2_fwd_fp8_kernel(Fp8Args a) {
+  using G = Fp8Geom<D, NW>;
+  constexpr int TSZ = G::TSZ, NS = 3, CPW = G::CPW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+  Fp8Wave<D, CAUSAL, NW> w;
+  w.init(a, smem);
+  const int nt = w.nt;
+
+  auto tile = [&](int j, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int key0 = j * G::BC;
+    if (CAUSAL && key0 > w.q_w + 31) return;     // above this wave's diagonal
+    f32x16 sc[G::KB];
+    i32x8 pk[G::PS];
+    float alpha;
+    w.scores(smem + S * TSZ, sc);
+    // keep the phases apart: hoisting the P.V operand reads above the softmax
+    // would hold them in registers beside the scores
+    __builtin_amdgcn_sched_barrier(0);
+    if (w.masked(key0)) w.template softmax<true>(sc, key0, pk, alpha);
+    else w.template softmax<false>(sc, key0, pk, alpha);
+    w.rescale(alpha);
+    __builtin_amdgcn_sched_barrier(0);
+    w.pv(smem + (NS + S) * TSZ, pk);
     // an explicit use keeps the compiler from sinking these products into
     // the next tile, past its scores, with P and V^T held live meanwhile
 #pragma unroll
-    for (int db = 0; db < DB; ++db) use_vgprs(acc[db]);
+    for (int db = 0; db < G::DB; ++db) use_vgprs(w.acc[db]);
   };
-
   auto step = [&](int j, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;    // == j % NS
     // this wave's copies of tile j are complete once at most those of tile
-    // j + 1 (two instructions) remain
-    if (j + 1 < nt) FA2_WAIT_VMCNT(2); else FA2_WAIT_VMCNT(0);
+    // j + 1 (2 CPW instructions) remain
+    if (j + 1 < nt) FA2_WAIT_VMCNT(2 * CPW); else FA2_WAIT_VMCNT(0);
     // every wave's copies of tile j have landed and every wave is done with
     // tile j - 1, whose stage the copy of tile j + 2 refills
     __syncthreads();
-    if (j + NS - 1 < nt) dma(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    if (j + NS - 1 < nt) {
+      constexpr int S2 = (S + NS - 1) % NS;
+      w.copy(w.kr, j + NS - 1, S2 * TSZ);
+      w.copy(w.vr, j + NS - 1, (NS + S2) * TSZ);
+    }
     tile(j, stage_tag);
   };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  dma(0, I0{});
-  if (nt > 1) dma(1, I1{});
+  w.copy(w.kr, 0, 0);
+  w.copy(w.vr, 0, NS * TSZ);
+  if (nt > 1) {
+    w.copy(w.kr, 1, TSZ);
+    w.copy(w.vr, 1, (NS + 1) * TSZ);
+  }
   // the Q loads were issued before the copies: wait for them only
-  if (nt > 1) FA2_WAIT_VMCNT(4); else FA2_WAIT_VMCNT(2);
+  if (nt > 1) FA2_WAIT_VMCNT(4 * CPW); else FA2_WAIT_VMCNT(2 * CPW);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) use_vgprs(qf[s]);
+  for (int s = 0; s < G::KS; ++s) use_vgprs(w.qf[s]);
   int j = 0;
   for (; j + NS <= nt; j += NS) {
     step(j, I0{});
@@ -370,30 +465,7 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
   }
   if (j < nt) step(j, I0{});
   if (j + 1 < nt) step(j + 1, I1{});
-
-  // ---- epilogue: O = acc * (dv / l) in bf16, LSE = (m + log2 l - 8) ln 2 -----
-  const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((uint16_t*)a.o + head_off), 0, head_bytes * 2u, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t lsr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-  const int row = q_w + lr;
-  const float l = sum_halves(l_run);
-  const float sc_o = a.dv / l;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 w;
-      w[0] = Elem<true>::pack(acc[db][4 * i + 0] * sc_o, acc[db][4 * i + 1] * sc_o);
-      w[1] = Elem<true>::pack(acc[db][4 * i + 2] * sc_o, acc[db][4 * i + 3] * sc_o);
-      const int d = 32 * db + 8 * i + 4 * lh;
-      __builtin_amdgcn_raw_buffer_store_b64(w, orr, (uint32_t)(row * D * 2 + d * 2), 0, 0);
-    }
-  }
-  if (lh == 0) {
-    const float lse = (m_run + log2f(l) - kFp8Shift) * 0.69314718055994530942f;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lsr, (uint32_t)(row * 4), 0, 0);
-  }
+  w.store(a);
 }
 
 }  // namespace fa2

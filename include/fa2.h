@@ -141,10 +141,10 @@ int fa2_fwd_check(const void* q, const void* k, const void* v, const void* o, co
  * O and LSE are those of the definition at the top of this file applied to
  * the dequantised inputs, except for one rounding step: the probabilities
  * enter the P.V product as E4M3 values.  Per tile of 8192/d keys (64 keys at
- * d = 128, 128 at d = 64, in key order) and per row, P = 2^(8 + c*s - m)
+ * d = 128, 128 at d = 64, in key order) and per row, P = 2^(6 + c*s - m)
  * with c = scale * descale_q * descale_k * log2(e) and m the row's
  * reference max, which moves to the tile's max only when that exceeds it
- * by more than 0.75, is rounded to the nearest E4M3 value (ties to even);
+ * by more than 2.75, is rounded to the nearest E4M3 value (ties to even);
  * the row sum l takes the unrounded P.  Both products accumulate in fp32.
  * Errors: as for fa2_fwd; scale, any descale, or c not finite in float32
  * is FA2_ERR_ARG.

@@ -33,8 +33,11 @@ The pages give no FP8 scheme.  READINGS:
       and LSE = m + ln l - shift ln 2.
   F4  The reference m of a row follows R6 with threshold tau: it moves to the
       tile max only when that exceeds m by more than tau (or m is still
-      -inf).  So 2^shift P <= 2^shift e^tau; shift = 8 with tau = 0.75 ln 2
-      keeps it at most 2^8.75 ~= 430.5 < 448.
+      -inf).  So 2^shift P <= 2^shift e^tau; shift = 6 with tau = 2.75 ln 2
+      keeps it at most 2^8.75 ~= 430.5 < 448, while values down to 2^-12 of
+      the reference stay normal E4M3 numbers.  (With shift 8 and tau 0.75 ln 2
+      the reference of a 32-row group moved in about half of the tiles of
+      N(0,1) inputs, against 6 % here, at the same error.)
   F5  Rounding to E4M3 saturates: magnitudes above 448 give 448.  F4 keeps P
       below that; the rule only makes the rounding function total.
 
@@ -67,9 +70,9 @@ __all__ = [
 #: largest finite E4M3 magnitude (reading F1): 1.75 * 2^8
 E4M3_MAX = 448.0
 #: P is scaled by 2^P_SHIFT before rounding (reading F3)
-P_SHIFT = 8
+P_SHIFT = 6
 #: threshold of the lazy reference in base-2 units (reading F4); tau = TAU_LOG2 * ln 2
-TAU_LOG2 = 0.75
+TAU_LOG2 = 2.75
 
 
 def e4m3_decode(codes) -> np.ndarray:

@@ -2,9 +2,9 @@
 
 Two kinds of inputs:
 
-* Exact inputs (workloads.make_exact_fp8): every 2^8 P lies on the E4M3 grid,
+* Exact inputs (workloads.make_exact_fp8): every 2^6 P lies on the E4M3 grid,
   so the tiled model of oracle/fp8.py (tiles of 8192/d keys, reference
-  threshold 0.75 in base 2, P scaled by 2^8) involves no rounding besides the
+  threshold 2.75 in base 2, P scaled by 2^6) involves no rounding besides the
   kernel's fp32 accumulation and the bf16 output.  Bound per element:
       |O - O_model| <= 2^-8 |O_model| + 2^-11 sum_j P~_j |v_j| / l
   (half an ulp of bf16 is at most 2^-8 |x|; the accumulation term is about 16x

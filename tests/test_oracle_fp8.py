@@ -173,7 +173,8 @@ def two_key_example(bc):
     v8 = np.array([[0xC0], [0x38]], dtype=np.uint8)
     # two rows so that the shapes agree: row 1 is a copy of row 0's query
     q8 = np.vstack([q8, q8])
-    return attention_online_fp8(q8, k8, v8, 1.0, 1.0, 1.0, False, scale, bc)
+    # explicit shift 8 and threshold 0.75 (base 2), which the numbers below follow
+    return attention_online_fp8(q8, k8, v8, 1.0, 1.0, 1.0, False, scale, bc, tau=0.75 * math.log(2.0), shift=8)
 
 
 def test_online_fp8_hand_example():

@@ -28,7 +28,7 @@ DEFAULT_KERNELS = (
     + [f"void fa2::fa2_bwd_dkdv_kernel<{b}, 64, {c}, fa2::BwdTile<4, 1> >(fa2::BwdArgs)" for b in B for c in B]
     + [f"void fa2::fa2_bwd_dq_kernel<{b}, 64, false, fa2::BwdTile<8, 2>, 0>(fa2::BwdArgs)" for b in B]
     + [f"void fa2::fa2_bwd_dq_kernel<{b}, 64, true, fa2::BwdTile<4, 2>, 4>(fa2::BwdArgs)" for b in B]
-    + [f"void fa2::fa2_fwd_fp8_kernel<{d}, {c}>(fa2::Fp8Args)" for d in (64, 128) for c in B]
+    + [f"void fa2::fa2_fwd_fp8_kernel<{d}, {c}, 4, 3>(fa2::Fp8Args)" for d in (64, 128) for c in B]
 )
 
 # variant 0 resolves to these tile variants (the list above follows them)

@@ -74,8 +74,10 @@ def test_fp8_exact_inputs_recipe():
     (q8, k8, v8), (dq, dk, dv), scale = W.make_exact_fp8(1, 2, 100, 128, seed=6)
     assert (dq, dk) == (0.5, 0.25)
     assert set(q8.unique().tolist()) <= {0x00, 0x38, 0xB8} and set(k8.unique().tolist()) <= {0x00, 0x38, 0xB8}
-    assert ((q8 != 0).sum(-1) == 8).all() and ((k8 != 0).sum(-1) == 16).all()
+    nq = (q8 != 0).sum(-1)
+    assert ((nq == 6) | (nq == 7)).all() and (nq == 6).any() and (nq == 7).any()
+    assert ((k8 != 0).sum(-1) == 16).all()
     q = q8.view(torch.float8_e4m3fn).double() * dq
     k = k8.view(torch.float8_e4m3fn).double() * dk
     t = scale * (q @ k.transpose(-1, -2)) / math.log(2.0)
-    assert (t - t.round()).abs().max() < 1e-12 and t.abs().max() <= 8
+    assert (t - t.round()).abs().max() < 1e-12 and t.abs().max() <= 7

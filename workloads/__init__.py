@@ -23,13 +23,13 @@ FP8 inputs (8-bit E4M3 codes with one float32 descale factor per tensor):
     PyTorch's CPU cast to float8_e4m3fn (nearest even), read back as bytes;
   * ``make_exact_fp8``: inputs on which the FP8 pass has no rounding besides
     summation order and the output cast.  Each head has 16 random positions
-    out of d; every K row holds +-1 at all 16, every Q row +-1 at 8 of them
-    (code 0x38 is 1.0, 0xB8 is -1.0, the rest 0x00); descales 1/2 and 1/4 and
-    scale 8 ln 2 make scale * q.k * log2(e) an integer in [-8, 8], so every
-    2^8 P lies on the E4M3 grid (2^-8 .. 2^8).  V is drawn as in
-    ``make_inputs_fp8``.  Draw order: V (as above, seed), then from
-    default_rng(EXACT_SEED_OFFSET + seed) the head positions, the Q
-    positions, the Q signs and the K signs.
+    out of d; every K row holds +-1 at all 16, every Q row +-1 at 6 or 7 of
+    them (code 0x38 is 1.0, 0xB8 is -1.0, the rest 0x00); descales 1/2 and
+    1/4 and scale 8 ln 2 make scale * q.k * log2(e) an integer in [-7, 7],
+    so every 2^6 P lies on the E4M3 grid (2^-8 .. 2^8), away from the
+    midpoints.  V is drawn as in ``make_inputs_fp8``.  Draw order: V (as
+    above, seed), then from default_rng(EXACT_SEED_OFFSET + seed) the head
+    positions, the Q positions, the Q signs, the Q counts and the K signs.
 """
 
 from __future__ import annotations
@@ -190,17 +190,21 @@ def make_exact_fp8(B: int, H: int, N: int, d: int, seed: int):
     v8, dv = _to_e4m3(v)
     rng = np.random.default_rng(EXACT_SEED_OFFSET + seed)
     head_pos = np.argsort(rng.random((B, H, 1, d)), axis=-1)[..., :16]          # [B, H, 1, 16]
-    q_pick = np.argsort(rng.random((B, H, N, 16)), axis=-1)[..., :8]            # 8 of the 16
+    q_pick = np.argsort(rng.random((B, H, N, 16)), axis=-1)[..., :7]            # 7 of the 16
     q_pos = np.take_along_axis(np.broadcast_to(head_pos, (B, H, N, 16)), q_pick, axis=-1)
-    q_sign = rng.integers(0, 2, size=(B, H, N, 8))
+    q_sign = rng.integers(0, 2, size=(B, H, N, 7))
+    q_count = 6 + rng.integers(0, 2, size=(B, H, N, 1))                          # keep 6 or 7
     k_sign = rng.integers(0, 2, size=(B, H, N, 16))
 
-    def codes(pos, sign):
+    def codes(pos, sign, keep=None):
         c = np.zeros((B, H, N, d), dtype=np.uint8)
-        np.put_along_axis(c, pos, np.where(sign == 1, 0xB8, 0x38).astype(np.uint8), axis=-1)
+        val = np.where(sign == 1, 0xB8, 0x38).astype(np.uint8)
+        if keep is not None:
+            val = np.where(keep, val, 0).astype(np.uint8)
+        np.put_along_axis(c, pos, val, axis=-1)
         return torch.from_numpy(c).contiguous()
 
-    q8 = codes(q_pos, q_sign)
+    q8 = codes(q_pos, q_sign, np.arange(7)[None, None, None, :] < q_count)
     k8 = codes(np.broadcast_to(head_pos, (B, H, N, 16)), k_sign)
     return (q8, k8, v8), (0.5, 0.25, dv), EXACT_FP8_SCALE
 
