@@ -104,15 +104,16 @@ static_assert(kNumVariants == 9, "variant table");
 // Measured on MI355X (same box, alternating runs): d = 128 runs the
 // hand-scheduled loop, persistent for non-causal N % 256 == 0 (headline shape
 // 0.471 ms against 0.483 for one workgroup per item and 0.52-0.53 for variant
-// 4; N = 16384 causal 1.84 against 1.88 ms); non-causal d = 64 runs 128-key
-// tiles in a 2-stage ring with 4 operand reads ahead (variant 3); causal
-// d = 64 runs 4-wave workgroups, two per CU, on a 2-stage ring of 64-key
-// tiles (variant 2: twice the workgroups balance the triangular work).
+// 4; N = 16384 causal 1.84 against 1.88 ms); d = 64 runs 128-key tiles in a
+// 2-stage ring with 4 operand reads ahead (variant 3), causal too: on
+// B=4, H=16, N=1024, causal, 23.5 against 25.2 us per call for the 4-wave
+// workgroups of variant 2 (bench runs alternating over three rounds).
 constexpr int kSchedVariant = 8;
 int default_variant(int bf16, int d, int causal) {
   (void)bf16;
+  (void)causal;
   if (d == 128) return kSchedVariant;
-  return causal ? 2 : 3;
+  return 3;
 }
 
 // compute units of the current device (one persistent workgroup each)
@@ -209,13 +210,22 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
 // ---- FP8 forward ------------------------------------------------------------
 
 typedef void (*fp8_fn)(fa2::Fp8Args);
-// 4-wave workgroups, three per CU: measured on MI355X against 8-wave
-// workgroups (two waves per SIMD of one workgroup), bitwise-equal results:
-// 0.348 against 0.408 ms on B=8, H=32, N=2048, d=128; 0.116 against 0.122 ms
-// on B=2, H=16, N=4096, d=128, causal; 20.3 against 21.3 us at d = 64.
-constexpr int kW = fa2::kFp8Waves, kOcc = fa2::kFp8Occupancy;
-const fp8_fn kFp8[2][2] = {{fa2::fa2_fwd_fp8_kernel<64, false, kW, kOcc>, fa2::fa2_fwd_fp8_kernel<64, true, kW, kOcc>},
-                           {fa2::fa2_fwd_fp8_kernel<128, false, kW, kOcc>, fa2::fa2_fwd_fp8_kernel<128, true, kW, kOcc>}};
+// Kernel per (d, causal).  Measured on MI355X with the configurations timed
+// in turn over six rounds (medians; outputs bitwise equal across them):
+// non-causal, 4-wave workgroups three per CU: 324 against 368 us for 8-wave
+// workgroups (two waves per SIMD of one workgroup) on B=8, H=32, N=2048,
+// d=128, and within 2 % at d = 64; causal, 8-wave workgroups: 99.6 against
+// 110.4 us (4-wave, three per CU) on B=2, H=16, N=4096, d=128, and 18.4
+// against 19.3 us at d = 64.
+struct Fp8Kernel {
+  fp8_fn fn;
+  int waves;   // waves per workgroup (32 query rows each)
+};
+const Fp8Kernel kFp8[2][2] = {
+    {{fa2::fa2_fwd_fp8_kernel<64, false, 4, 3>, 4}, {fa2::fa2_fwd_fp8_kernel<64, true, 8, 2>, 8}},
+    {{fa2::fa2_fwd_fp8_kernel<128, false, 4, 3>, 4}, {fa2::fa2_fwd_fp8_kernel<128, true, 8, 2>, 8}}};
+// the smallest query block of the FP8 kernels (bounds the grid)
+constexpr int kFp8MinRows = 128;
 
 // c = scale * descale_q * descale_k * log2(e), in double, then float
 float fp8_exponent_scale(float scale, float dq, float dk) {
@@ -236,7 +246,7 @@ int check_fp8(const void* q, const void* k, const void* v, const void* o, const 
   if (bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
   const uint64_t elems = bh * (uint64_t)N * (uint64_t)d;
   if (elems >= (1ull << 62)) return FA2_ERR_SHAPE;
-  if (((uint64_t)N + fa2::kFp8Rows - 1) / fa2::kFp8Rows * bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
+  if (((uint64_t)N + kFp8MinRows - 1) / kFp8MinRows * bh > (uint64_t)INT32_MAX) return FA2_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u)
     return FA2_ERR_ALIGN;
   const size_t ib = (size_t)elems;         // one byte per input element
@@ -261,11 +271,13 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.lse = lse;
   a.BH = (int)bh;
   a.N = N;
-  a.nqb = (N + fa2::kFp8Rows - 1) / fa2::kFp8Rows;
+  const Fp8Kernel& kern = kFp8[d == 128][causal];
+  const int rows = 32 * kern.waves;
+  a.nqb = (N + rows - 1) / rows;
   a.c = fp8_exponent_scale(scale, dq, dk);
   a.dv = dv;
   const uint64_t blocks = (uint64_t)a.nqb * bh;
-  hipLaunchKernelGGL(kFp8[d == 128][causal], dim3((unsigned)blocks), dim3(64 * kW), 0, stream, a);
+  hipLaunchKernelGGL(kern.fn, dim3((unsigned)blocks), dim3(64 * kern.waves), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return FA2_ERR_LAUNCH;
   return FA2_OK;
 }

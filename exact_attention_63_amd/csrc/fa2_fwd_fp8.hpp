@@ -72,9 +72,6 @@ struct Fp8Args {
 constexpr int kFp8TileBytes = 8192;  // one K (or V) tile: 8192 / d keys
 constexpr float kFp8Lazy = 2.75f;    // reference threshold, base 2
 constexpr float kFp8Shift = 6.f;     // P is scaled by 2^6 before rounding to E4M3
-constexpr int kFp8Waves = 4;         // waves per workgroup of the launched kernel
-constexpr int kFp8Rows = 32 * kFp8Waves;   // its query rows per workgroup
-constexpr int kFp8Occupancy = 3;     // its waves per SIMD: three workgroups per CU
 
 // XOR swizzle of the 16-byte chunks of a [key][d] row of d bytes (d = 128: 8
 // chunks, d = 64: 4 chunks).  d = 128: bits 1, 3, 2 of the row give bits 1, 2,
@@ -393,10 +390,11 @@ struct Fp8Wave {
 
 // Tile by tile: S, softmax and P.V of tile j between two barriers, the copy
 // of tile j + 2 in flight meanwhile (3-stage ring of K and V tiles).  NW
-// waves per workgroup: with 4, two workgroups share a CU and their barriers
-// are independent, so one's softmax overlaps the other's matrix products.
-// WPE: waves per SIMD the register budget is sized for (3: at most 168
-// VGPRs, three 4-wave workgroups per CU).
+// waves per workgroup; WPE: waves per SIMD the register budget is sized for.
+// With NW = 4 and WPE = 3 (at most 168 VGPRs) three workgroups share a CU and
+// their barriers are independent, so one's softmax overlaps another's
+// matrix products; with NW = 8 and WPE = 2 one workgroup of 256 rows fills
+// it.
 template <int D, bool CAUSAL, int NW, int WPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 void fa2_fwd_fp8_kernel(Fp8Args a) {
