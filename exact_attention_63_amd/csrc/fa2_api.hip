@@ -353,17 +353,16 @@ const char* const kBwdVariantNames[kNumBwdVariants] = {"default", "dkdv_w4_occ1"
                                                        "dkdv_w4_occ1_dq_w4_look4",
                                                        "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4"};
 
-// Measured on MI355X (bench.py --backward, alternating runs on one box): at
-// d = 128 the P hand-off between the two waves of a SIMD pipelined across
-// query tiles is fastest (headline shape 2.23-2.24 ms per call against
-// 2.35-2.40 for the unpipelined hand-off, variant 2; N = 16384 causal 8.5-8.6
-// against 9.4 ms; 2.95 for variant 1); at d = 64 variant 1 (0.125-0.129 ms
-// against 0.130-0.133 for variants 2 and 3), and for causal d = 64 variant 3,
-// whose 4-wave dQ workgroups balance the triangular work (0.095 against
-// 0.103 ms).
+// Measured on MI355X with the variants timed in turn over five rounds
+// (medians, one process): the P hand-off between the two waves of a SIMD
+// pipelined across query tiles (variant 4) is fastest everywhere: headline
+// shape 2.13 ms against 2.25 (variant 2) and 2.97 (variant 1); N = 4096
+// causal 0.593 against 0.631 and 0.778 ms; B=4, H=16, N=1024, d=64, 98.0 us
+// against 111-112 us for variants 1-3, and causal 85.7 against 88.8-96.7 us.
 int default_bwd_variant(int d, int causal) {
-  if (d == 128) return 4;
-  return causal ? 3 : 1;
+  (void)d;
+  (void)causal;
+  return 4;
 }
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* lse,

@@ -225,8 +225,7 @@ int fa2_bwd_bf16(const void* q, const void* k, const void* v, const void* o, con
  *   4 "dkdv_w8_pipe_occ2_ring3_q64_look2_dq_look4": the P hand-off of
  *     variant 2 pipelined across query tiles, one barrier per iteration,
  *     dK/dV MFMAs 2 operand reads ahead.
- * The default is variant 4 for d = 128, variant 1 for non-causal d = 64 and
- * variant 3 for causal d = 64.
+ * The default is variant 4.
  * Returns FA2_ERR_ARG for an unknown variant.
  */
 int fa2_bwd_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -22,11 +22,9 @@ DEFAULT_KERNELS = (
     + [f"void fa2::fa2_fwd_sched_persist_kernel<{b}>(fa2::Args)" for b in B]
     + [f"void fa2::fa2_fwd_kernel<{b}, 64, {c}, fa2::Tile<8, 1, 4, 2, 2, 4, 0> >(fa2::Args)" for b in B for c in B]
     + [f"void fa2::fa2_bwd_delta_kernel<{b}, {d}>(fa2::BwdArgs, long long)" for b in B for d in (64, 128)]
-    + [f"void fa2::fa2_bwd_dkdv_pipe_kernel<{b}, 128, {c}, 2>(fa2::BwdArgs)" for b in B for c in B]
-    + [f"void fa2::fa2_bwd_dq_kernel<{b}, 128, {c}, fa2::BwdTile<8, 2>, 4>(fa2::BwdArgs)" for b in B for c in B]
-    + [f"void fa2::fa2_bwd_dkdv_kernel<{b}, 64, {c}, fa2::BwdTile<4, 1> >(fa2::BwdArgs)" for b in B for c in B]
-    + [f"void fa2::fa2_bwd_dq_kernel<{b}, 64, false, fa2::BwdTile<8, 2>, 0>(fa2::BwdArgs)" for b in B]
-    + [f"void fa2::fa2_bwd_dq_kernel<{b}, 64, true, fa2::BwdTile<4, 2>, 4>(fa2::BwdArgs)" for b in B]
+    + [f"void fa2::fa2_bwd_dkdv_pipe_kernel<{b}, {d}, {c}, 2>(fa2::BwdArgs)" for b in B for d in (64, 128) for c in B]
+    + [f"void fa2::fa2_bwd_dq_kernel<{b}, {d}, {c}, fa2::BwdTile<8, 2>, 4>(fa2::BwdArgs)"
+       for b in B for d in (64, 128) for c in B]
     + [f"void fa2::fa2_fwd_fp8_kernel<{d}, false, 4, 3>(fa2::Fp8Args)" for d in (64, 128)]
     + [f"void fa2::fa2_fwd_fp8_kernel<{d}, true, 8, 2>(fa2::Fp8Args)" for d in (64, 128)]
 )
