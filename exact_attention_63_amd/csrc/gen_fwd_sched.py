@@ -264,7 +264,10 @@ def copy_setup(a):
     so it lands in the ring stage of its index).  Without a next item the
     next descriptors are the current ones: the copies then fetch tiles 0-2
     of the same head again into stages no wave reads, which keeps four
-    copies in every interval.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
+    copies in every interval.  A tile index t - T that is not below T (only
+    when T < 3, so without a next item) becomes tile 0: the tile offset goes
+    in soffset, which the buffer's range check does not cover, so every copy
+    must stay inside the head.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
     for jr, cur, nxt, off in ((S_J3, S_KDESC, S_NKD, S_SOFF), (S_J2, S_VDESC, S_NVD, S_VSOFF)):
         a(f"s_cmp_eq_u32 s{jr}, s{S_T}")
         a(f"s_cselect_b64 s[{cur}:{cur + 1}], s[{nxt}:{nxt + 1}], s[{cur}:{cur + 1}]")
@@ -272,6 +275,8 @@ def copy_setup(a):
         a(f"s_cmp_lt_u32 s{jr}, s{S_T}")
         a(f"s_cselect_b32 s{S_TMP}, 0, s{S_T}")
         a(f"s_sub_u32 s{S_TMP}, s{jr}, s{S_TMP}")
+        a(f"s_cmp_lt_u32 s{S_TMP}, s{S_T}")
+        a(f"s_cselect_b32 s{S_TMP}, s{S_TMP}, 0")
         a(f"s_lshl_b32 s{off}, s{S_TMP}, 14")
 
 

@@ -1,11 +1,14 @@
-"""A small instruction-level emulator for the generated gfx950 main loop of the
-scheduled forward kernel (exact_attention_63_amd/csrc/fa2_fwd_sched.inc).
+"""A small instruction-level emulator for the generated gfx950 main loops of the
+scheduled forward kernels (exact_attention_63_amd/csrc/fa2_fwd_sched.inc and
+fa2_fwd_fp8_sched.inc).
 
 Test infrastructure only: it executes the assembly text of one workgroup (all
 its waves, barrier by barrier) on the CPU and checks, besides the values:
 
   * every register read waits for the load that fills it (lgkmcnt / vmcnt);
-  * the wait states the hardware does not enforce (MFMA result -> VALU,
+  * the wait states the hardware does not enforce (MFMA result -> VALU: 12
+    after a 32x32x16 bf16/f16 MFMA, 20 after a 32x32x64 FP8 one, the counts
+    the compiler inserts;
     VALU -> MFMA source, transcendental result -> VALU, VALU -> permlane,
     M0 -> LDS copy), counted in issue slots (s_nop n = n + 1 slots);
   * an LDS operand buffer is refilled only after two further MFMAs;
@@ -23,6 +26,15 @@ kernel sources):
     first); D register r of lane l is D[8(r//4) + 4(l//32) + r%4][l%32].
   * ds_read_b64_tr_b16: in each 16-lane group, output lane i, element e is
     element i%4 of the 8 bytes addressed by lane 4e + i//4 of the group.
+  * v_mfma_f32_32x32x64_f8f6f4 (E4M3 operands): lane l holds A[l%32][32(l//32)+b]
+    and B[32(l//32)+b][l%32] in byte b = 0..31 of its eight registers (the
+    pairing of A and B bytes is what matters: both take the same slot); D as
+    above.
+  * ds_read_b64_tr_b8: in each 16-lane group, output lane i, byte e is byte
+    i%8 of the 8 bytes addressed by lane 2e + i//8 of the group.
+  * v_cvt_pk_fp8_f32 d, a, b [op_sel:[0,0,1]]: a, b rounded to E4M3 (nearest
+    even) into bytes 0, 1 (2, 3 with op_sel) of d, the other half of d kept;
+    a magnitude above 448 is an error here (the kernel never produces one).
   * buffer_load_dwordx4 ... offen lds: lane l copies 16 bytes from
     soffset + voffset[l] of the buffer to LDS address M0 + 16 l; bytes past the
     buffer's size read as zero.
@@ -33,6 +45,7 @@ from __future__ import annotations
 import re
 
 import numpy as np
+import torch
 
 LANES = 64
 
@@ -74,6 +87,24 @@ def _unpack16(regs, bf16):
     return el.astype(np.uint16).view(np.float16).astype(np.float32).T.copy()
 
 
+def _e4m3_values(regs):
+    """(n regs, 64) uint32 -> (64, 4n) float64: the E4M3 values of the bytes,
+    byte b of register r at index 4r + b."""
+    by = np.ascontiguousarray(regs.T).view(np.uint8)               # (64, 4n), little endian
+    t = torch.from_numpy(by.copy()).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _e4m3_rne(x):
+    """float32 values -> E4M3 codes (uint32), round to nearest even; the
+    kernel never converts a magnitude above 448 (or a NaN)."""
+    x = np.asarray(x, dtype=np.float32)
+    if np.isnan(x).any() or (np.abs(x) > 448).any():
+        raise EmuError("E4M3 conversion of a value outside [-448, 448]")
+    t = torch.from_numpy(x.copy()).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().astype(np.uint32)
+
+
 VREG = re.compile(r"^v(\d+)$|^v\[(\d+):(\d+)\]$")
 SREG = re.compile(r"^s(\d+)$|^s\[(\d+):(\d+)\]$")
 
@@ -111,7 +142,9 @@ def parse(text):
             labels[line[:-1]] = len(ins)
             continue
         op, _, rest = line.partition(" ")
-        args = [a.strip() for a in rest.split(",")] if rest else []
+        mods = re.findall(r"op_sel:\[[^\]]*\]", rest)       # modifiers whose lists hold commas
+        rest = re.sub(r"\s*op_sel:\[[^\]]*\]", "", rest)
+        args = ([a.strip() for a in rest.split(",")] if rest else []) + mods
         ins.append((op, args, line))
     addr, a = [], 0
     for op, args, line in ins:
@@ -159,6 +192,7 @@ class Wave:
         self.valu_w = np.full(256, -10**9)  # slot of the last VALU write
         self.trans_w = np.full(256, -10**9)
         self.mfma_w = np.full(256, -10**9)
+        self.mfma_need = np.zeros(256, dtype=np.int64)   # wait states after that MFMA
         self.mfma_dst = {}                 # reg -> dst range of the last MFMA that wrote it
         self.mfma_rd = np.full(256, -1)    # MFMA count at the last MFMA source read
         self.n_mfma = 0
@@ -177,8 +211,10 @@ class Wave:
         if self.pending[rng].any():
             self.err(f"v{lo}..v{hi} {what} while a load into it is pending")
         now = self.slot
-        if (now - self.mfma_w[rng] <= 12).any() and not mfma:
-            self.err("MFMA result read by a non-MFMA instruction within 12 wait states")
+        close = (now - self.mfma_w[rng] <= self.mfma_need[rng])
+        if close.any() and not mfma:
+            n = int(self.mfma_need[rng][close].max())
+            self.err(f"MFMA result read by a non-MFMA instruction within {n} wait states")
         if (now - self.trans_w[rng] < 2).any():
             self.err("transcendental result read within 1 wait state")
         if mfma and (now - self.valu_w[rng] < 3).any():
@@ -191,8 +227,10 @@ class Wave:
         rng = slice(lo, hi + 1)
         if self.pending[rng].any():
             self.err(f"v{lo}..v{hi} written while a load into it is pending")
-        if kind != "mfma" and (self.slot - self.mfma_w[rng] <= 12).any():
-            self.err("register written within 12 wait states of an MFMA that wrote it")
+        close = (self.slot - self.mfma_w[rng] <= self.mfma_need[rng])
+        if kind != "mfma" and close.any():
+            n = int(self.mfma_need[rng][close].max())
+            self.err(f"register written within {n} wait states of an MFMA that wrote it")
         if kind in ("valu", "trans"):
             self.valu_w[rng] = self.slot
             if kind == "trans":
@@ -319,13 +357,13 @@ class Wave:
             if a not in prog.addr_to_index:
                 self.err("s_setpc_b64 to an address that is not an instruction")
             nxt = prog.addr_to_index[a]
-        elif op == "ds_read_b128" or op == "ds_read_b64_tr_b16":
+        elif op in ("ds_read_b128", "ds_read_b64_tr_b16", "ds_read_b64_tr_b8"):
             self.ds_read(op, args)
         elif op == "buffer_load_dwordx4" and "lds" in line:
             self.lds_copy(args, line)
         elif op == "buffer_load_dwordx4":
             self.vgpr_load(args, line)
-        elif op.startswith("v_mfma_f32_32x32x16_"):
+        elif op.startswith("v_mfma_f32_32x32x16_") or op == "v_mfma_f32_32x32x64_f8f6f4":
             self.mfma(op, args)
         elif op.startswith("v_"):
             self.valu(op, args)
@@ -380,6 +418,20 @@ class Wave:
             na[32:] = xb[:32]
             nb[:32] = xa[32:]
             self.v[a], self.v[b] = na, nb
+        elif op == "v_cvt_pk_fp8_f32":
+            a, b = self.fsrc(args[1]), self.fsrc(args[2])
+            hi = "op_sel:[0,0,1]" in args[3:]
+            dlo, _ = vrange(args[0])
+            old = self.rd_v(dlo, dlo)[0].copy()
+            word = _e4m3_rne(a) | (_e4m3_rne(b) << 8)
+            self.wr_v(dlo, dlo, "valu")
+            self.v[dlo] = (old & 0x0000FFFF) | (word << 16) if hi else (old & 0xFFFF0000) | word
+        elif op == "v_cndmask_b32":
+            if args[3] != "vcc":
+                self.err("v_cndmask_b32 must select on vcc")
+            x0, x1 = _u32(self.fsrc(args[1])), _u32(self.fsrc(args[2]))
+            self.wr_v(*vrange(args[0]), "valu")
+            self.v[vrange(args[0])[0]] = np.where(self.vcc, x1, x0)
         elif op in ("v_cmp_lt_f32", "v_cmp_neq_f32"):
             if args[0] != "vcc":
                 self.err("compare must write vcc")
@@ -390,19 +442,26 @@ class Wave:
             self.err("unsupported VALU instruction")
 
     def mfma(self, op, args):
-        bf16 = op.endswith("bf16")
+        fp8 = op == "v_mfma_f32_32x32x64_f8f6f4"
+        nreg = 8 if fp8 else 4            # A / B registers per lane
+        kw = 32 if fp8 else 8             # k slots per lane half
+        need = 20 if fp8 else 12          # wait states before a VALU may read the result
         dlo, dhi = vrange(args[0])
         alo, ahi = vrange(args[1])
         blo, bhi = vrange(args[2])
-        if dhi - dlo != 15 or ahi - alo != 3 or bhi - blo != 3:
+        if dhi - dlo != 15 or ahi - alo != nreg - 1 or bhi - blo != nreg - 1:
             self.err("operand sizes")
-        a = _unpack16(self.rd_v(alo, ahi, mfma=True), bf16)   # (64, 8)
-        b = _unpack16(self.rd_v(blo, bhi, mfma=True), bf16)
-        A = np.zeros((32, 16), dtype=np.float32)
-        B = np.zeros((16, 32), dtype=np.float32)
+        if fp8:
+            a = _e4m3_values(self.rd_v(alo, ahi, mfma=True))   # (64, 32)
+            b = _e4m3_values(self.rd_v(blo, bhi, mfma=True))
+        else:
+            a = _unpack16(self.rd_v(alo, ahi, mfma=True), op.endswith("bf16"))   # (64, 8)
+            b = _unpack16(self.rd_v(blo, bhi, mfma=True), op.endswith("bf16"))
+        A = np.zeros((32, 2 * kw), dtype=np.float64)
+        B = np.zeros((2 * kw, 32), dtype=np.float64)
         for half in range(2):
-            A[:, 8 * half:8 * half + 8] = a[32 * half:32 * half + 32]
-            B[8 * half:8 * half + 8, :] = b[32 * half:32 * half + 32].T
+            A[:, kw * half:kw * half + kw] = a[32 * half:32 * half + 32]
+            B[kw * half:kw * half + kw, :] = b[32 * half:32 * half + 32].T
         if args[3] == "0":
             C = np.zeros((32, 32), dtype=np.float32)
         else:
@@ -416,8 +475,8 @@ class Wave:
                 self.err("VALU result read as srcC within 2 wait states")
             for r in range(clo, chi + 1):
                 w = self.mfma_dst.get(r)
-                if self.slot - self.mfma_w[r] < 12 and w != (dlo, dhi):
-                    self.err("srcC from a different MFMA within 12 wait states")
+                if self.slot - self.mfma_w[r] < self.mfma_need[r] and w != (dlo, dhi):
+                    self.err(f"srcC from a different MFMA within {self.mfma_need[r]} wait states")
             C = self.acc_to_mat(self.v[clo:chi + 1])
         D = (A.astype(np.float64) @ B.astype(np.float64) + C).astype(np.float32)
         for r in (range(alo, ahi + 1)):
@@ -429,10 +488,11 @@ class Wave:
         # a destination still counted by an earlier MFMA's result window is fine
         # only for the same accumulation chain
         for r in range(dlo, dhi + 1):
-            if self.slot - self.mfma_w[r] < 12 and self.mfma_dst.get(r) != (dlo, dhi):
-                self.err("MFMA writes registers of a different MFMA within 12 wait states")
+            if self.slot - self.mfma_w[r] < self.mfma_need[r] and self.mfma_dst.get(r) != (dlo, dhi):
+                self.err(f"MFMA writes registers of a different MFMA within {self.mfma_need[r]} wait states")
         self.v[dlo:dhi + 1] = self.mat_to_acc(D)
         self.mfma_w[dlo:dhi + 1] = self.slot
+        self.mfma_need[dlo:dhi + 1] = need
         for r in range(dlo, dhi + 1):
             self.mfma_dst[r] = (dlo, dhi)
 
@@ -474,6 +534,13 @@ class Wave:
             raw[l] = self.emu.lds[a:a + nbytes]
         if op == "ds_read_b128":
             data = raw.view(np.uint32).T.copy()            # (4, 64)
+        elif op == "ds_read_b64_tr_b8":
+            out = np.zeros((LANES, 8), dtype=np.uint8)
+            for g in range(4):
+                for i in range(16):
+                    for e in range(8):
+                        out[16 * g + i, e] = raw[16 * g + 2 * e + i // 8, i % 8]
+            data = out.view(np.uint32).T.copy()            # (2, 64)
         else:
             el = raw.view(np.uint16)                        # (64, 4)
             out = np.zeros((LANES, 4), dtype=np.uint16)
@@ -523,8 +590,12 @@ class Wave:
             g = soff + int(voff[l])
             if g % 16:
                 self.err("unaligned copy source")
-            if g + 16 <= len(buf):
-                src[l] = np.frombuffer(buf, dtype=np.uint8, count=16, offset=g)
+            if g < 0 or g + 16 > len(buf):
+                # the loops put the tile offset in soffset, which the range
+                # check of a raw buffer does not cover: every copy must stay
+                # inside the buffer by construction
+                self.err(f"copy source {g} outside the buffer of {len(buf)} bytes")
+            src[l] = np.frombuffer(buf, dtype=np.uint8, count=16, offset=g)
         dst = self.m0
         if dst < 0 or dst + 1024 > self.emu.lds_size or dst % 1024:
             self.err(f"LDS copy destination {dst} out of range")
