@@ -29,7 +29,8 @@
 // v[176:177], Q lane offset v185; K and V buffer descriptors s[40:43],
 // s[44:47], c s48, tile count s49, this wave's LDS copy address s52, the next
 // item's K, V, Q descriptors s[56:59], s[60:63], s[64:67], its Q block offset
-// s68 and whether there is one s69.  It clobbers v[96:159],
+// s68 and whether there is one s69, the tile shift past the last full tile
+// s72 and the whole tiles the copies may fetch s73.  It clobbers v[96:159],
 // v[180:FA2_SCHED_REG_END) but v185, a few SGPRs, m0, vcc and scc.
 #pragma once
 
@@ -137,18 +138,22 @@ __device__ __forceinline__ u32x32 sched_load_q(__amdgpu_buffer_rsrc_t qr, const 
 // the workgroup has synchronised after every wave waited for its copies.
 // With nx.has != 0 the loop leaves the next item's tiles there (the next
 // loop's barriers publish them), its Q fragments in q32 and its K and V
-// descriptors in kr and vr; without, nx holds the current descriptors.
+// descriptors in kr and vr (nsub = ntv = ntiles); without, nx holds the
+// current descriptors, nsub = 0 and ntv is the number of whole tiles of the
+// head: the loop's last copies leave K(t) for 3 <= t <= ntiles + 2 and V(t)
+// for 2 <= t <= ntiles + 1 with t < ntv in ring stage t % 4, and every copy
+// has landed when it returns.
 template <bool BF16>
 __device__ __forceinline__ void sched_loop(f32x16& acc0, f32x16& acc1, f32x16& acc2, f32x16& acc3, float& m_run,
                                            float& l_run, u32x32& q32, __amdgpu_buffer_rsrc_t& kr,
                                            __amdgpu_buffer_rsrc_t& vr, const SchedWave& w, float c, int ntiles,
-                                           const SchedNext& nx) {
+                                           const SchedNext& nx, int nsub, int ntv) {
 #define FA2_SCHED_OPERANDS                                                                                 \
   : "+{v[32:47]}"(acc0), "+{v[48:63]}"(acc1), "+{v[64:79]}"(acc2), "+{v[80:95]}"(acc3), "={v178}"(m_run), \
     "={v179}"(l_run), "+{v[0:31]}"(q32), "+{s[40:43]}"(kr), "+{s[44:47]}"(vr)                              \
   : "{v[160:167]}"(w.ka), "{v[168:175]}"(w.va), "{v[176:177]}"(w.dsrc), "{v185}"(w.qoff), "{s48}"(c),     \
     "{s49}"(ntiles), "{s52}"(w.m0b), "{s[56:59]}"(nx.k), "{s[60:63]}"(nx.v), "{s[64:67]}"(nx.q),           \
-    "{s68}"(nx.qoff), "{s69}"(nx.has)                                                                      \
+    "{s68}"(nx.qoff), "{s69}"(nx.has), "{s72}"(nsub), "{s73}"(ntv)                                      \
   : FA2_SCHED_CLOBBERS
   if constexpr (BF16) asm volatile(FA2_SCHED_BF16 FA2_SCHED_OPERANDS);
   else asm volatile(FA2_SCHED_F16 FA2_SCHED_OPERANDS);
@@ -257,88 +262,97 @@ void fa2_fwd_sched_kernel(Args a) {
   f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
   float m_run = -INFINITY, l_run = 0.f;
 
+  const int ntv = N / BC;   // whole tiles of the head
   if (nfull > 0) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     const SchedNext none{kr, vr, qr, 0u, 0u};
-    sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, nfull, none);
+    sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, nfull, none, 0, ntv);
   }
 
   // ---- tiles that need a mask: diagonal (causal) or past N (ragged) --------
+  // At most 4 (a 256-row block crosses the diagonal in 4 tiles; a ragged
+  // sequence ends in one), so tile j owns ring stage j % 4.  The loop's last
+  // copies fetched K(j) for 3 <= j <= nfull + 2 and V(j) for 2 <= j <= nfull + 1
+  // where j is a whole tile; the rest are copied here, before one barrier.
   if (nfull < nt) {
     __syncthreads();   // the loop's last P.V reads finished in every wave
     for (int j = nfull; j < nt; ++j) {
-      const int key0 = j * BC;
+      const bool k_have = nfull > 0 && j >= 3 && j <= nfull + 2 && j < ntv;
+      const bool v_have = nfull > 0 && j >= 2 && j <= nfull + 1 && j < ntv;
+      const int st = (j % NS) * TSZ;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        lds_dma16(kr, smem + (2 * wave + k) * 1024, w.dsrc[k], j * TSZ);
-        lds_dma16(vr, smem + VOFF + (2 * wave + k) * 1024, w.dsrc[k], j * TSZ);
+        if (!k_have) lds_dma16(kr, smem + st + (2 * wave + k) * 1024, w.dsrc[k], j * TSZ);
+        if (!v_have) lds_dma16(vr, smem + VOFF + st + (2 * wave + k) * 1024, w.dsrc[k], j * TSZ);
       }
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (!(CAUSAL && key0 > q_w + 31)) {
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int j = nfull; j < nt; ++j) {
+      const int key0 = j * BC;
+      if (CAUSAL && key0 > q_w + 31) continue;     // above this wave's diagonal
+      const uint32_t st = (uint32_t)((j % NS) * TSZ);
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk)
+      for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const u32x4 kf = lds_load_b128(w.ka[dk] + kb * 32 * KROW);
-            s[kb] = E::mfma(kf, qfrag(dk), s[kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 kf = lds_load_b128(w.ka[dk] + st + kb * 32 * KROW);
+          s[kb] = E::mfma(kf, qfrag(dk), s[kb]);
+        }
+      // scale, mask (keys past N, keys after the query), row max
+      const int q = q_w + lr;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool vis = key < N && (!CAUSAL || key <= q);
+          s[kb][r] = vis ? s[kb][r] * c : -INFINITY;
+          mx = fmaxf(mx, s[kb][r]);
+        }
+      mx = max_halves(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // never -inf - -inf
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+      u32x4 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            p[t] = __builtin_amdgcn_exp2f(s[kb][8 * h + t] - m_use);
+            rs += p[t];
           }
-        // scale, mask (keys past N, keys after the query), row max
-        const int q = q_w + lr;
-        float mx = -INFINITY;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) pf[kb][h][t] = E::pack(p[2 * t], p[2 * t + 1]);
+        }
+      l_run = l_run * alpha + rs;
+      if (__any(alpha != 1.f)) {
+        acc0 *= alpha;
+        acc1 *= alpha;
+        acc2 *= alpha;
+        acc3 *= alpha;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x16& acc = db == 0 ? acc0 : db == 1 ? acc1 : db == 2 ? acc2 : acc3;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool vis = key < N && (!CAUSAL || key <= q);
-            s[kb][r] = vis ? s[kb][r] * c : -INFINITY;
-            mx = fmaxf(mx, s[kb][r]);
+          for (int h = 0; h < 2; ++h) {
+            const int roff = (32 * kb + 16 * h) * KROW;
+            const u32x2 lo = lds_tr16_at(w.va[2 * db] + st + roff);
+            const u32x2 hi = lds_tr16_at(w.va[2 * db + 1] + st + roff);
+            acc = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kb][h], acc);
           }
-        mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // never -inf - -inf
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float rs = 0.f;
-        u32x4 pf[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            float p[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              p[t] = __builtin_amdgcn_exp2f(s[kb][8 * st + t] - m_use);
-              rs += p[t];
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) pf[kb][st][t] = E::pack(p[2 * t], p[2 * t + 1]);
-          }
-        l_run = l_run * alpha + rs;
-        if (__any(alpha != 1.f)) {
-          acc0 *= alpha;
-          acc1 *= alpha;
-          acc2 *= alpha;
-          acc3 *= alpha;
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          f32x16& acc = db == 0 ? acc0 : db == 1 ? acc1 : db == 2 ? acc2 : acc3;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-              const int roff = (32 * kb + 16 * st) * KROW;
-              const u32x2 lo = lds_tr16_at(w.va[2 * db] + roff);
-              const u32x2 hi = lds_tr16_at(w.va[2 * db + 1] + roff);
-              acc = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kb][st], acc);
-            }
-        }
       }
-      __syncthreads();
     }
   }
 
@@ -404,7 +418,7 @@ void fa2_fwd_sched_persist_kernel(Args a) {
     }
     f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
     float m_run, l_run;
-    sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, ntiles, nx);
+    sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, ntiles, nx, ntiles, ntiles);
     sched_store<BF16>(a, bh, qblk * BR + wave * 32, lane, acc0, acc1, acc2, acc3, m_run, l_run);
     if (nxt < 0) break;
     bh = nxt / nqb;

@@ -106,6 +106,8 @@ S_NQOFF = 68
 S_HASN = 69
 S_TMP = 70
 S_VSOFF = 71            # byte offset of the V tile this interval copies
+S_NSUB = 72             # past the last full tile T-1 a copy fetches tile t - s72 (T: the next item's, 0: this head's)
+S_NTV = 73              # tiles below s73 may be fetched (whole tiles of the head the copies read)
 SGPR_CLOBBER = [S_J, S_SOFF, S_TM1, S_J2, S_J3, S_TMP, S_VSOFF]
 
 
@@ -258,24 +260,28 @@ def rescale(a, name):
 def copy_setup(a):
     """Descriptors and tile offsets of this interval's copies, without
     branches.  Interval j copies K of tile j+3 and V of tile j+2.  Past the
-    item's last tile T-1 the same slots copy the next item's tiles 0-2 (K)
-    and 0-1 (V): at j+3 == T (j+2 == T) the K (V) descriptor becomes the
-    next item's, and tile t >= T is the next item's tile t - T (T % 4 == 0,
-    so it lands in the ring stage of its index).  Without a next item the
-    next descriptors are the current ones: the copies then fetch tiles 0-2
-    of the same head again into stages no wave reads, which keeps four
-    copies in every interval.  A tile index t - T that is not below T (only
-    when T < 3, so without a next item) becomes tile 0: the tile offset goes
-    in soffset, which the buffer's range check does not cover, so every copy
-    must stay inside the head.  s{S_J2} = j + 2, s{S_J3} = j + 3."""
+    item's last full tile T-1 the same slots copy either
+      * the next item's tiles 0-2 (K) and 0-1 (V) (persistent workgroups,
+        s{S_NSUB} = T): at j+3 == T (j+2 == T) the K (V) descriptor becomes
+        the next item's, and tile t >= T is the next item's tile t - T
+        (T % 4 == 0, so it lands in the ring stage of its index); or
+      * tile t of the same head (one item per workgroup, s{S_NSUB} = 0, the
+        next descriptors being the current ones): the masked tiles after the
+        loop (a causal workgroup's diagonal) find K(T..T+2) and V(T..T+1) in
+        their ring stages.
+    A tile index not below s{S_NTV} (not a whole tile of the head) becomes
+    tile 0, copied into a stage no wave reads: the tile offset goes in
+    soffset, which the buffer's range check does not cover, so every copy
+    stays inside the head.  Every interval issues four copies.
+    s{S_J2} = j + 2, s{S_J3} = j + 3."""
     for jr, cur, nxt, off in ((S_J3, S_KDESC, S_NKD, S_SOFF), (S_J2, S_VDESC, S_NVD, S_VSOFF)):
         a(f"s_cmp_eq_u32 s{jr}, s{S_T}")
         a(f"s_cselect_b64 s[{cur}:{cur + 1}], s[{nxt}:{nxt + 1}], s[{cur}:{cur + 1}]")
         a(f"s_cselect_b64 s[{cur + 2}:{cur + 3}], s[{nxt + 2}:{nxt + 3}], s[{cur + 2}:{cur + 3}]")
         a(f"s_cmp_lt_u32 s{jr}, s{S_T}")
-        a(f"s_cselect_b32 s{S_TMP}, 0, s{S_T}")
+        a(f"s_cselect_b32 s{S_TMP}, 0, s{S_NSUB}")
         a(f"s_sub_u32 s{S_TMP}, s{jr}, s{S_TMP}")
-        a(f"s_cmp_lt_u32 s{S_TMP}, s{S_T}")
+        a(f"s_cmp_lt_u32 s{S_TMP}, s{S_NTV}")
         a(f"s_cselect_b32 s{S_TMP}, s{S_TMP}, 0")
         a(f"s_lshl_b32 s{off}, s{S_TMP}, 14")
 

@@ -48,7 +48,7 @@ def bits16(x, dtype):
     return t.view(torch.int16).numpy().view(np.uint16), t.to(torch.float64).numpy()
 
 
-def init_wave(w, wave, qbits, N, qblk, T, c):
+def init_wave(w, wave, qbits, N, qblk, T, c, ntv=None):
     """Register state the C++ side establishes before the loop."""
     lanes = np.arange(64)
     lr, lh = lanes % 32, lanes // 32
@@ -76,10 +76,13 @@ def init_wave(w, wave, qbits, N, qblk, T, c):
     wave.s[GEN.S_C] = int(np.float32(c).view(np.uint32))
     wave.s[GEN.S_T] = T
     wave.s[GEN.S_M0B] = 2048 * w
-    # no next item: its descriptors are the current ones
+    # no next item: its descriptors are the current ones; past tile T-1 the
+    # copies fetch this head's whole tiles
     wave.s[GEN.S_NKD] = 1
     wave.s[GEN.S_NVD] = 2
     wave.s[GEN.S_HASN] = 0
+    wave.s[GEN.S_NSUB] = 0
+    wave.s[GEN.S_NTV] = ntv if ntv is not None else T
 
 
 def run_workgroup(dtype, q, k, v, qblk, T, scale, text=None, hits=None):
@@ -251,6 +254,8 @@ def test_consecutive_items(dtype):
             wave.v[GEN.R_QOFF] = (lanes % 32) * 256 + 16 * (lanes // 32)
             _desc(wave.s, GEN.S_KDESC, 11 + 3 * h, N * 256)
             _desc(wave.s, GEN.S_VDESC, 12 + 3 * h, N * 256)
+            wave.s[GEN.S_NSUB] = T          # persistent: past tile T-1, the next item's tiles
+            wave.s[GEN.S_NTV] = T
             if i + 1 == len(items):
                 _desc(wave.s, GEN.S_NKD, 11 + 3 * h, N * 256)
                 _desc(wave.s, GEN.S_NVD, 12 + 3 * h, N * 256)
@@ -292,3 +297,48 @@ def test_consecutive_items(dtype):
         o_ref, l_ref = oracle.attention_3pass(*f64[h], False, scale, rows=rows)
         assert np.abs(o - o_ref).max() <= TOL_O[dtype], (i, np.abs(o - o_ref).max())
         assert np.abs(lse - l_ref).max() <= 1e-3, i
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+def test_tiles_after_the_loop(T):
+    """One item whose head has 4 whole tiles after the loop's T (a causal
+    workgroup's diagonal tiles): the loop's last copies leave K of tiles
+    T..T+2 and V of tiles T..T+1 (those of them from tile 3 and 2 on) in
+    their ring stages, and its result covers the first T tiles."""
+    rng = np.random.default_rng(30 + T)
+    N = 64 * (T + 4)
+    q, k, v = (rng.standard_normal((N, D), dtype=np.float32) for _ in range(3))
+    qb, q64 = bits16(q, "bf16")
+    kb, k64 = bits16(k, "bf16")
+    vb, v64 = bits16(v, "bf16")
+    scale = 1 / math.sqrt(D)
+    text = "\n".join(GEN.block("bf16"))
+    emu = Emulator([text] * 8, 128 * 1024, {1: kb.tobytes(), 2: vb.tobytes()})
+    for w, wave in enumerate(emu.waves):
+        init_wave(w, wave, qb, N, 0, T, scale * math.log2(math.e), ntv=N // 64)
+    for tile in range(min(T, 3)):
+        halves = [(kb, tile * GEN.TSZ)] + ([(vb, GEN.VOFF + tile * GEN.TSZ)] if tile < 2 else [])
+        for src, base in halves:
+            for r in range(64):
+                for p in range(16):
+                    row, ch = tile * 64 + r, p ^ swz(r)
+                    dst = base + r * 256 + 16 * p
+                    emu.lds[dst:dst + 16] = np.frombuffer(src[row, 8 * ch:8 * ch + 8].tobytes(), dtype=np.uint8)
+    emu.run()
+    for src, first, last, base in ((kb, 3, T + 2, 0), (vb, 2, T + 1, GEN.VOFF)):
+        for t in range(max(T, first), last + 1):
+            st = base + (t % 4) * GEN.TSZ
+            for r in range(64):
+                for p in range(16):
+                    ch = p ^ swz(r)
+                    want = np.frombuffer(src[t * 64 + r, 8 * ch:8 * ch + 8].tobytes(), dtype=np.uint8)
+                    assert np.array_equal(emu.lds[st + r * 256 + 16 * p:st + r * 256 + 16 * p + 16], want), (t, r, p)
+    # the loop's own result: the first T tiles of keys
+    lse = np.zeros(256)
+    for w, wave in enumerate(emu.waves):
+        m = wave.v[GEN.R_M].view(np.float32).astype(np.float64)
+        l = wave.v[GEN.R_L].view(np.float32).astype(np.float64)
+        lse[32 * w:32 * w + 32] = (m[:32] + np.log2(l[:32] + l[32:])) * math.log(2)
+    n = min(256, 64 * T)
+    _, l_ref = oracle.attention_3pass(q64[:64 * T], k64[:64 * T], v64[:64 * T], False, scale, rows=np.arange(n))
+    assert np.abs(lse[:n] - l_ref).max() <= 1e-3
