@@ -39,7 +39,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "exact_attention_63_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_sched.hpp", "fa2_fwd_sched.inc")]
-FP8_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_fp8.hpp")]
+FP8_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_fwd_kernel.hpp", "fa2_fwd_fp8.hpp",
+                                                       "fa2_fwd_fp8_sched.hpp", "fa2_fwd_fp8_sched.inc")]
 PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
 
 
@@ -50,9 +51,11 @@ def kernel_identity(w, variant: int = 0) -> str:
     import exact_attention_63_amd as fa2
     h = hashlib.sha256()
     if w.dtype == "fp8":
+        vi = variant or fa2.lib().fa2_fp8_default_variant(w.d, int(w.causal))
         for src in FP8_KERNEL_SOURCES:
             with open(src, "rb") as f:
                 h.update(f.read())
+        h.update(fa2.fp8_variant_name(vi).encode())
         h.update(f"{w.dtype}/{w.d}/{int(w.causal)}".encode())
         return h.hexdigest()[:16]
     vi = variant or fa2.default_variant(0 if w.dtype == "fp16" else 1, w.d, w.causal)
@@ -327,7 +330,7 @@ def run_workload(w, steps, warmup, variant=0):
         o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
 
         def step():
-            fa2.forward_fp8(q, k, v, *desc, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            fa2.forward_fp8(q, k, v, *desc, causal=w.causal, scale=w.scale, out=o, lse=lse, variant=variant)
     else:
         q, k, v = (t.cuda() for t in workload_inputs(w))
         o = torch.empty_like(q)

@@ -18,7 +18,7 @@ import math
 import os
 
 __all__ = [
-    "forward", "forward_fp8", "backward", "bwd_num_variants", "bwd_variant_name", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
+    "forward", "forward_fp8", "fp8_num_variants", "fp8_variant_name", "backward", "bwd_num_variants", "bwd_variant_name", "lib", "lib_path", "status_string", "num_variants", "variant_name", "version",
     "default_variant",
     "FA2_OK", "FA2_ERR_NULL", "FA2_ERR_SHAPE", "FA2_ERR_UNSUPPORTED", "FA2_ERR_ALIGN",
     "FA2_ERR_ARG", "FA2_ERR_ALIAS", "FA2_ERR_LAUNCH", "FA2_DTYPE_FP16", "FA2_DTYPE_BF16",
@@ -53,6 +53,11 @@ EXPORTS = {
     "fa2_fwd_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
     "fa2_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "fa2_fwd_fp8_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F]),
+    "fa2_fwd_fp8_variant": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _I]),
+    "fa2_fwd_fp8_variant_check": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _I]),
+    "fa2_fp8_num_variants": (_I, []),
+    "fa2_fp8_variant_name": (ctypes.c_char_p, [_I]),
+    "fa2_fp8_default_variant": (_I, [_I, _I]),
     "fa2_bwd": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P, _I]),
     "fa2_bwd_fp16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
     "fa2_bwd_bf16": (_I, [_P] * 10 + [_I, _I, _I, _I, _I, _F, _P]),
@@ -192,12 +197,13 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, *, varian
 
 
 def forward_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, causal: bool = False,
-                scale: float | None = None, *, out=None, lse=None):
+                scale: float | None = None, *, out=None, lse=None, variant: int = 0):
     """FP8 attention forward: returns (O [B,H,N,d] bfloat16, LSE [B,H,N] float32).
 
     q, k, v: contiguous CUDA (ROCm) uint8 tensors [B, H, N, d] of OCP E4M3
     codes (a float8_e4m3fn tensor viewed as uint8), d in {64, 128}; the
     inputs are decode(q) * descale_q etc.  scale defaults to 1/sqrt(d).
+    variant 0 calls fa2_fwd_fp8; any other calls fa2_fwd_fp8_variant.
     Enqueued on the current stream of q's device; the call does not
     synchronise.  An empty problem returns the empty outputs without a
     library call.
@@ -233,12 +239,24 @@ def forward_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, c
         return out, lse
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        rc = lib().fa2_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               B, H, N, d, int(bool(causal)), float(scale), float(descale_q),
-                               float(descale_k), float(descale_v), stream)
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                int(bool(causal)), float(scale), float(descale_q), float(descale_k), float(descale_v), stream)
+        if variant == 0:
+            rc, where = lib().fa2_fwd_fp8(*args), "fa2_fwd_fp8"
+        else:
+            rc, where = lib().fa2_fwd_fp8_variant(*args, int(variant)), "fa2_fwd_fp8_variant"
     if rc != FA2_OK:
-        raise Fa2Error(rc, "fa2_fwd_fp8")
+        raise Fa2Error(rc, where)
     return out, lse
+
+
+def fp8_num_variants() -> int:
+    return lib().fa2_fp8_num_variants()
+
+
+def fp8_variant_name(variant: int) -> str | None:
+    name = lib().fa2_fp8_variant_name(variant)
+    return None if name is None else name.decode()
 
 
 def bwd_num_variants() -> int:

@@ -20,6 +20,7 @@ LIB = os.path.join(PKG, "libfa2.so")
 SOURCES = [os.path.join(PKG, "csrc", "fa2_api.hip")]
 HEADERS = [os.path.join(PKG, "csrc", "fa2_fwd_kernel.hpp"), os.path.join(PKG, "csrc", "fa2_fwd_sched.hpp"),
            os.path.join(PKG, "csrc", "fa2_fwd_sched.inc"), os.path.join(PKG, "csrc", "fa2_fwd_fp8.hpp"),
+           os.path.join(PKG, "csrc", "fa2_fwd_fp8_sched.hpp"), os.path.join(PKG, "csrc", "fa2_fwd_fp8_sched.inc"),
            os.path.join(ROOT, "include", "fa2.h")]
 ARCH = "gfx950"
 

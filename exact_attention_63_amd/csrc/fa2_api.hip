@@ -17,6 +17,7 @@
 #include "fa2_fwd_roles.hpp"
 #include "fa2_fwd_sched.hpp"
 #include "fa2_fwd_fp8.hpp"
+#include "fa2_fwd_fp8_sched.hpp"
 
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -224,8 +225,21 @@ struct Fp8Kernel {
 const Fp8Kernel kFp8[2][2] = {
     {{fa2::fa2_fwd_fp8_kernel<64, false, 4, 3>, 4}, {fa2::fa2_fwd_fp8_kernel<64, true, 8, 2>, 8}},
     {{fa2::fa2_fwd_fp8_kernel<128, false, 4, 3>, 4}, {fa2::fa2_fwd_fp8_kernel<128, true, 8, 2>, 8}}};
+// the hand-scheduled d = 128 kernel (8 waves x 32 rows), per causal
+const Fp8Kernel kFp8Sched[2] = {{fa2::fa2_fwd_fp8_sched_kernel<false>, 8}, {fa2::fa2_fwd_fp8_sched_kernel<true>, 8}};
 // the smallest query block of the FP8 kernels (bounds the grid)
 constexpr int kFp8MinRows = 128;
+// FP8 variants: 0 = default, 1 = tile by tile (fa2_fwd_fp8_kernel), 2 = the
+// scheduled loop (d = 128 only)
+constexpr int kNumFp8Variants = 3;
+const char* const kFp8VariantNames[kNumFp8Variants] = {"default", "tile_by_tile", "sched_ring4"};
+// Measured on MI355X with the variants timed in turn (same box, medians,
+// outputs bitwise equal): causal d = 128, B=2, H=16, N=4096: 86.7 us for the
+// scheduled loop against 100.5 us tile by tile; non-causal B=8, H=32,
+// N=2048: 329 against 315 us (the scheduled loop's start and end of every
+// 256-row item cost more than the tile-by-tile kernel's three 4-wave
+// workgroups per CU, which overlap theirs; at N=8192 the two are within 1 %).
+int default_fp8_variant(int d, int causal) { return d == 128 && causal ? 2 : 1; }
 
 // c = scale * descale_q * descale_k * log2(e), in double, then float
 float fp8_exponent_scale(float scale, float dq, float dk) {
@@ -233,13 +247,15 @@ float fp8_exponent_scale(float scale, float dq, float dk) {
 }
 
 int check_fp8(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
-              int N, int d, int causal, float scale, float dq, float dk, float dv) {
+              int N, int d, int causal, float scale, float dq, float dk, float dv, int variant) {
   if (causal != 0 && causal != 1) return FA2_ERR_ARG;
+  if (variant < 0 || variant >= kNumFp8Variants) return FA2_ERR_ARG;
   if (!finite_bits(scale) || !finite_bits(dq) || !finite_bits(dk) || !finite_bits(dv)) return FA2_ERR_ARG;
   if (!finite_bits(fp8_exponent_scale(scale, dq, dk))) return FA2_ERR_ARG;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
   if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (variant == 2 && d != 128) return FA2_ERR_UNSUPPORTED;
   // one head of o (2-byte elements) must be addressable with 32-bit byte offsets
   if ((uint64_t)N * (uint64_t)d * 2u >= (1ull << 32)) return FA2_ERR_SHAPE;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
@@ -259,8 +275,8 @@ int check_fp8(const void* q, const void* k, const void* v, const void* o, const 
 }
 
 int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-            int causal, float scale, float dq, float dk, float dv, hipStream_t stream) {
-  const int st = check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv);
+            int causal, float scale, float dq, float dk, float dv, hipStream_t stream, int variant) {
+  const int st = check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, dq, dk, dv, variant);
   if (st != FA2_OK) return st;
   const uint64_t bh = (uint64_t)B * (uint64_t)H;
   fa2::Fp8Args a;
@@ -271,7 +287,8 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.lse = lse;
   a.BH = (int)bh;
   a.N = N;
-  const Fp8Kernel& kern = kFp8[d == 128][causal];
+  const int vi = variant == 0 ? default_fp8_variant(d, causal) : variant;
+  const Fp8Kernel& kern = vi == 2 ? kFp8Sched[causal] : kFp8[d == 128][causal];
   const int rows = 32 * kern.waves;
   a.nqb = (N + rows - 1) / rows;
   a.c = fp8_exponent_scale(scale, dq, dk);
@@ -496,14 +513,35 @@ FA2_EXPORT int fa2_fwd_check(const void* q, const void* k, const void* v, const 
 FA2_EXPORT int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int N, int d, int causal, float scale, float descale_q, float descale_k,
                            float descale_v, hipStream_t stream) {
-  return run_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, stream);
+  return run_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, stream, 0);
+}
+
+FA2_EXPORT int fa2_fwd_fp8_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                   int H, int N, int d, int causal, float scale, float descale_q,
+                                   float descale_k, float descale_v, hipStream_t stream, int variant) {
+  return run_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, stream, variant);
 }
 
 FA2_EXPORT int fa2_fwd_fp8_check(const void* q, const void* k, const void* v, const void* o,
                                  const float* lse, int B, int H, int N, int d, int causal, float scale,
                                  float descale_q, float descale_k, float descale_v) {
-  return check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v);
+  return check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, 0);
 }
+
+FA2_EXPORT int fa2_fwd_fp8_variant_check(const void* q, const void* k, const void* v, const void* o,
+                                         const float* lse, int B, int H, int N, int d, int causal,
+                                         float scale, float descale_q, float descale_k, float descale_v,
+                                         int variant) {
+  return check_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, variant);
+}
+
+FA2_EXPORT int fa2_fp8_num_variants(void) { return kNumFp8Variants; }
+
+FA2_EXPORT const char* fa2_fp8_variant_name(int variant) {
+  return variant >= 0 && variant < kNumFp8Variants ? kFp8VariantNames[variant] : nullptr;
+}
+
+FA2_EXPORT int fa2_fp8_default_variant(int d, int causal) { return default_fp8_variant(d, causal); }
 
 FA2_EXPORT int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,

@@ -162,6 +162,41 @@ int fa2_fwd_fp8_check(const void* q, const void* k, const void* v, const void* o
                       float descale_q, float descale_k, float descale_v);
 
 /*
+ * fa2_fwd_fp8_variant -- fa2_fwd_fp8 with an explicit kernel, for tuning and
+ * for tests that compare the kernels.  variant 0 is the default that
+ * fa2_fwd_fp8 uses (fa2_fp8_default_variant says which); the others are
+ * described by fa2_fp8_variant_name():
+ *   1 "tile_by_tile": score, softmax and P.V of one tile between two
+ *     barriers, the copy of a later tile in flight;
+ *   2 "sched_ring4": d = 128 only (FA2_ERR_UNSUPPORTED otherwise): the
+ *     hand-scheduled loop, 8 waves of 32 rows, the softmax of tile j between
+ *     the P.V MFMAs of tile j-1 and the score MFMAs of tile j+1.
+ * The default is variant 2 for causal d = 128 and variant 1 otherwise.
+ * Every variant computes the same function, including where the reference
+ * moves; results agree to fp32 summation order.  Returns FA2_ERR_ARG for an
+ * unknown variant, otherwise as fa2_fwd_fp8.
+ */
+int fa2_fwd_fp8_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, int causal, float scale,
+                        float descale_q, float descale_k, float descale_v, hipStream_t stream,
+                        int variant);
+
+/* The argument validation of fa2_fwd_fp8_variant, without launching anything. */
+int fa2_fwd_fp8_variant_check(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, int B, int H, int N, int d, int causal, float scale,
+                              float descale_q, float descale_k, float descale_v, int variant);
+
+/* Number of FP8 variants (including the default, 0). */
+int fa2_fp8_num_variants(void);
+
+/* Static name of an FP8 variant ("default" for 0), or NULL when out of range. */
+const char* fa2_fp8_variant_name(int variant);
+
+/* The FP8 variant (>= 1) that variant 0 resolves to for head dimension d and
+ * causal (0/1); only d = 64 and 128 are meaningful. */
+int fa2_fp8_default_variant(int d, int causal);
+
+/*
  * fa2_bwd -- the backward pass: gradients of the forward pass's O with
  * respect to q, k and v, given the upstream gradient dO.
  *

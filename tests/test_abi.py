@@ -278,3 +278,28 @@ def test_python_fp8_binding_rejects_bad_tensors(lib):
         fa2.forward_fp8(x, x, x, 1.0, 1.0, 1.0)                  # CPU tensors
     with pytest.raises(ValueError):
         fa2.forward_fp8(x.float(), x.float(), x.float(), 1.0, 1.0, 1.0)
+
+
+def fvchk(variant, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=128, causal=0, scale=0.125, dq=0.01, dk=0.02, dv=0.5)
+    a.update(kw)
+    return fa2.lib().fa2_fwd_fp8_variant_check(*a.values(), variant)
+
+
+def test_fp8_variant_validation(lib):
+    n = fa2.fp8_num_variants()
+    assert n == 3
+    assert fa2.fp8_variant_name(0) == "default" and fa2.fp8_variant_name(n) is None
+    assert all(fa2.fp8_variant_name(i) for i in range(n)) and fa2.fp8_variant_name(-1) is None
+    for v in range(n):
+        assert fvchk(v) == fa2.FA2_OK
+        assert fvchk(v, N=0) == fa2.FA2_ERR_SHAPE
+    assert fvchk(n) == fa2.FA2_ERR_ARG and fvchk(-1) == fa2.FA2_ERR_ARG
+    assert fvchk(2, d=64) == fa2.FA2_ERR_UNSUPPORTED
+    assert fvchk(1, d=64) == fa2.FA2_OK
+    for d in (64, 128):
+        for causal in (0, 1):
+            assert fa2.lib().fa2_fp8_default_variant(d, causal) in (1, 2)
+    # variant 0 validates exactly as fa2_fwd_fp8_check
+    for kw in (dict(), dict(d=64, causal=1), dict(q=None), dict(dv=math.nan), dict(o=Q)):
+        assert fvchk(0, **kw) == fchk(**kw)

@@ -51,8 +51,8 @@ def tile_keys(d):
     return 8192 // d
 
 
-def gpu_fp8(q8, k8, v8, desc, causal, scale):
-    o, lse = fa2.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *desc, causal=causal, scale=scale)
+def gpu_fp8(q8, k8, v8, desc, causal, scale, variant=0):
+    o, lse = fa2.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *desc, causal=causal, scale=scale, variant=variant)
     torch.cuda.synchronize()
     og, lg = to_f64(o), to_f64(lse)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
@@ -85,9 +85,9 @@ def heads_of(B, H, heads):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
 
 
-def check_exact(q8, k8, v8, desc, causal, scale, heads=None, what=""):
+def check_exact(q8, k8, v8, desc, causal, scale, heads=None, what="", variant=0):
     B, H, N, d = q8.shape
-    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale)
+    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale, variant)
     worst = 0.0
     for b, h in heads_of(B, H, heads):
         args = (q8[b, h].numpy(), k8[b, h].numpy(), v8[b, h].numpy())
@@ -101,9 +101,9 @@ def check_exact(q8, k8, v8, desc, causal, scale, heads=None, what=""):
     print(f"{what}: worst error / bound {worst:.3f}", flush=True)
 
 
-def check_real(q8, k8, v8, desc, causal, scale, heads=None, what=""):
+def check_real(q8, k8, v8, desc, causal, scale, heads=None, what="", variant=0):
     B, H, N, d = q8.shape
-    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale)
+    og, lg = gpu_fp8(q8, k8, v8, desc, causal, scale, variant)
     d_km, d_mx, o_m = [], [], []
     for b, h in heads_of(B, H, heads):
         args = (q8[b, h].numpy(), k8[b, h].numpy(), v8[b, h].numpy())
@@ -197,3 +197,100 @@ def test_fp8_invalid_call_writes_nothing():
         fa2.forward_fp8(q, k, v, math.inf, 1.0, 1.0, out=o, lse=lse)
     torch.cuda.synchronize()
     assert (o == 7.0).all() and (lse == 7.0).all()
+
+
+# ---- the kernel variants (fa2_fwd_fp8_variant) ---------------------------------
+# 1: tile by tile; 2: the hand-scheduled d = 128 loop, whose full tiles run
+# in assembly and whose diagonal and tail tiles run the C++ steps of variant 1
+# from the ring stages the loop's last copies filled
+
+SCHED = [2]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [c for c in EXACT_CASES if c[3] == 128] + [
+    (1, 2, 512, 128, False), (1, 1, 192, 128, False), (1, 1, 128, 128, True), (2, 1, 2048, 128, True)])
+@pytest.mark.parametrize("variant", SCHED)
+def test_fp8_sched_exact_inputs(B, H, N, d, causal, variant):
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(B, H, N, d, seed=N + d)
+    check_exact(q8, k8, v8, desc, causal, scale, what=f"v{variant} exact B{B} H{H} N{N} causal={causal}",
+                variant=variant)
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 2, 700, False), (1, 2, 700, True), (1, 1, 1, False),
+                                          (1, 2, 1024, False), (2, 1, 333, True)])
+@pytest.mark.parametrize("variant", SCHED)
+def test_fp8_sched_realistic_inputs(B, H, N, causal, variant):
+    (q8, k8, v8), desc = W.make_inputs_fp8(B, H, N, 128, seed=N + 384)
+    check_real(q8, k8, v8, desc, causal, 1 / math.sqrt(128), what=f"v{variant} real B{B} H{H} N{N} causal={causal}",
+               variant=variant)
+
+
+@pytest.mark.parametrize("variant", SCHED)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_sched_reference_moves(causal, variant):
+    # per-key-row offsets on K: the reference moves inside the assembly loop
+    (q8, k8, v8), desc = W.make_inputs_fp8(1, 2, 1024, 128, seed=5, sigma=0.5, key_offset=(-4.0, 4.0))
+    check_real(q8, k8, v8, desc, causal, 1 / math.sqrt(128), what=f"v{variant} key offset causal={causal}",
+               variant=variant)
+    (q8, k8, v8), desc = W.make_inputs_fp8(1, 2, 1024, 128, seed=6)
+    check_real(q8, k8, v8, desc, causal, 4 / math.sqrt(128), what=f"v{variant} scale x4 causal={causal}",
+               variant=variant)
+
+
+@pytest.mark.parametrize("name", [n for n in sorted(W.FP8_WORKLOADS) if W.FP8_WORKLOADS[n].d == 128])
+@pytest.mark.parametrize("variant", SCHED)
+def test_fp8_sched_workloads(name, variant):
+    w = W.FP8_WORKLOADS[name]
+    (q8, k8, v8), desc = W.workload_inputs_fp8(w)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
+    check_real(q8, k8, v8, desc, w.causal, w.scale, heads=heads, what=f"v{variant} {name}", variant=variant)
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(w.B, w.H, w.N, w.d, seed=w.seed)
+    check_exact(q8, k8, v8, desc, w.causal, scale, heads=heads, what=f"v{variant} {name} exact inputs",
+                variant=variant)
+
+
+@pytest.mark.parametrize("variant", SCHED)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_variants_agree(causal, variant):
+    """The kernels take the same E4M3 decisions (the same reference rule in
+    fp32): their outputs differ by fp32 summation order at most, far below
+    the E4M3 rounding of P."""
+    (q8, k8, v8), desc = W.make_inputs_fp8(2, 4, 2048, 128, seed=31)
+    q, k, v = q8.cuda(), k8.cuda(), v8.cuda()
+    o1, l1 = fa2.forward_fp8(q, k, v, *desc, causal=causal, variant=1)
+    o2, l2 = fa2.forward_fp8(q, k, v, *desc, causal=causal, variant=variant)
+    o3, l3 = fa2.forward_fp8(q, k, v, *desc, causal=causal, variant=variant)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o3) and torch.equal(l2, l3), "the scheduled kernel is deterministic"
+    do = (o1.float() - o2.float()).abs()
+    assert (do <= 2.0 ** -7 * o1.float().abs() + 1e-5).all(), do.max().item()
+    assert (l1 - l2).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("variant", SCHED)
+def test_fp8_sched_d64_unsupported(variant):
+    (q8, k8, v8), desc = W.make_inputs_fp8(1, 1, 64, 64, seed=1)
+    with pytest.raises(fa2.Fa2Error) as ei:
+        fa2.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *desc, variant=variant)
+    assert ei.value.status == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("variant", SCHED)
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_fp8_sched_many_heads(variant, sign):
+    """More workgroups than CUs, a head count whose item total is not a
+    multiple of 8 (no XCD ranges), and a negative scale (every Q sign
+    flipped)."""
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(1, 130, 512, 128, seed=41)
+    heads = [(0, 0), (0, 64), (0, 127), (0, 128), (0, 129)]
+    check_exact(q8, k8, v8, desc, False, sign * scale, heads=heads, what=f"v{variant} chains sign {sign}",
+                variant=variant)
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 2, 1024), (1, 1, 1000), (2, 1, 576), (1, 1, 320), (1, 2, 4096)])
+def test_fp8_sched_causal_diagonal_tiles(B, H, N):
+    """Causal: every workgroup but the first ends with up to 4 diagonal tiles
+    that the loop's last copies fetched (whole tiles) or the code after the
+    loop copies (the ragged last one, or tiles below 3 / 2)."""
+    (q8, k8, v8), desc, scale = W.make_exact_fp8(B, H, N, 128, seed=N + 11)
+    check_exact(q8, k8, v8, desc, True, scale, what=f"sched diagonal B{B} H{H} N{N}", variant=2)

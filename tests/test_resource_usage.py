@@ -26,7 +26,8 @@ DEFAULT_KERNELS = (
     + [f"void fa2::fa2_bwd_dq_kernel<{b}, {d}, {c}, fa2::BwdTile<8, 2>, 4>(fa2::BwdArgs)"
        for b in B for d in (64, 128) for c in B]
     + [f"void fa2::fa2_fwd_fp8_kernel<{d}, false, 4, 3>(fa2::Fp8Args)" for d in (64, 128)]
-    + [f"void fa2::fa2_fwd_fp8_kernel<{d}, true, 8, 2>(fa2::Fp8Args)" for d in (64, 128)]
+    + ["void fa2::fa2_fwd_fp8_kernel<64, true, 8, 2>(fa2::Fp8Args)"]
+    + ["void fa2::fa2_fwd_fp8_sched_kernel<true>(fa2::Fp8Args)"]
 )
 
 # variant 0 resolves to these tile variants (the list above follows them)
@@ -65,10 +66,16 @@ def usage():
     return {dem: entries[m] for m, dem in zip(mangled, out.splitlines())}
 
 
+# FP8: variant 0 resolves to these (the list above follows them)
+DEFAULT_FP8 = {(128, 0): "tile_by_tile", (128, 1): "sched_ring4", (64, 0): "tile_by_tile", (64, 1): "tile_by_tile"}
+
+
 def test_defaults_are_the_listed_variants():
     for (d, causal), name in DEFAULT_FWD.items():
         for dt in (fa2.FA2_DTYPE_FP16, fa2.FA2_DTYPE_BF16):
             assert fa2.variant_name(fa2.default_variant(dt, d, causal)) == name
+    for (d, causal), name in DEFAULT_FP8.items():
+        assert fa2.fp8_variant_name(fa2.lib().fa2_fp8_default_variant(d, causal)) == name
 
 
 def test_default_kernels_do_not_spill(usage):
