@@ -360,8 +360,11 @@ struct Fp8Wave {
     }
   }
 
-  // O = acc * (dv / l) in bf16, LSE = (m + log2 l - 6) ln 2
-  __device__ __forceinline__ void store(const Fp8Args& a) const {
+  // O = acc * (dv / l) in bf16, LSE = (m + log2 l - 6) ln 2.  With d = 128, O
+  // goes through this wave's kStageBytes of LDS at stage (store_o128_staged;
+  // 4 KiB aligned, no longer read by any wave), else straight from the
+  // accumulators.
+  __device__ __forceinline__ void store(const Fp8Args& a, uint8_t* stage) const {
     const size_t head_off = (size_t)bh * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((uint16_t*)a.o + head_off), 0, (uint32_t)N * D * 2u, kBufferWord3);
@@ -370,15 +373,20 @@ struct Fp8Wave {
     const int row = q_w + lr;
     const float l = sum_halves(l_run);
     const float so = a.dv / l;
+    if constexpr (D == 128) {
+      store_o128_staged<true>(orr, q_w, lr + 32 * lh, acc[0], acc[1], acc[2], acc[3], so, stage);
+    } else {
+      (void)stage;
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db) {
+      for (int db = 0; db < G::DB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w;
-        w[0] = Elem<true>::pack(acc[db][4 * i + 0] * so, acc[db][4 * i + 1] * so);
-        w[1] = Elem<true>::pack(acc[db][4 * i + 2] * so, acc[db][4 * i + 3] * so);
-        const int d = 32 * db + 8 * i + 4 * lh;
-        __builtin_amdgcn_raw_buffer_store_b64(w, orr, (uint32_t)(row * D * 2 + d * 2), 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w[0] = Elem<true>::pack(acc[db][4 * i + 0] * so, acc[db][4 * i + 1] * so);
+          w[1] = Elem<true>::pack(acc[db][4 * i + 2] * so, acc[db][4 * i + 3] * so);
+          const int d = 32 * db + 8 * i + 4 * lh;
+          __builtin_amdgcn_raw_buffer_store_b64(w, orr, (uint32_t)(row * D * 2 + d * 2), 0, 0);
+        }
       }
     }
     if (lh == 0) {
@@ -400,7 +408,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_
 void fa2_fwd_fp8_kernel(Fp8Args a) {
   using G = Fp8Geom<D, NW>;
   constexpr int TSZ = G::TSZ, NS = 3, CPW = G::CPW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+  __shared__ __attribute__((aligned(4096))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+  static_assert(NW * kStageBytes <= 2 * NS * TSZ, "the ring holds the output staging");
   Fp8Wave<D, CAUSAL, NW> w;
   w.init(a, smem);
   const int nt = w.nt;
@@ -463,7 +472,12 @@ void fa2_fwd_fp8_kernel(Fp8Args a) {
   }
   if (j < nt) step(j, I0{});
   if (j + 1 < nt) step(j + 1, I1{});
-  w.store(a);
+  if constexpr (D == 128) {
+    __syncthreads();   // every wave is done with the ring: it stages the output
+    w.store(a, smem + (threadIdx.x >> 6) * kStageBytes);
+  } else {
+    w.store(a, nullptr);
+  }
 }
 
 }  // namespace fa2

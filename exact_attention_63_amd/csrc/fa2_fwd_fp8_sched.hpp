@@ -72,7 +72,8 @@ void fa2_fwd_fp8_sched_kernel(Fp8Args a) {
   using G = Fp8Geom<D, NW>;
   constexpr int TSZ = G::TSZ;
   static_assert(G::CPW == 1 && G::BC == 64 && G::BR == kFp8SchedRows, "the loop's geometry");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+  __shared__ __attribute__((aligned(4096))) uint8_t smem[2 * NS * TSZ];   // K stages, then V stages
+  static_assert(NW * kStageBytes <= 2 * NS * TSZ, "the ring holds the output staging");
 
   Fp8Wave<D, CAUSAL, NW> w;
   w.init(a, smem);
@@ -126,7 +127,8 @@ void fa2_fwd_fp8_sched_kernel(Fp8Args a) {
       w.pv(smem + (NS + j % NS) * TSZ, pk);
     }
   }
-  w.store(a);
+  __syncthreads();   // every wave is done with the ring: it stages the output
+  w.store(a, smem + (threadIdx.x >> 6) * kStageBytes);
 }
 
 }  // namespace fa2

@@ -116,6 +116,70 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
 }
 
+// LDS read of 16 bytes at a byte address of the workgroup's allocation.
+__device__ __forceinline__ u32x4 lds_load_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
+}
+
+// Bytes of LDS a wave needs to stage its output rows (store_o128_staged).
+constexpr int kStageBytes = 4096;
+
+// The O^T accumulators of a wave's 32 rows (d = 128; lane (row lr, half lh)
+// holds d = 32 db + 8 (r / 4) + 4 lh + r % 4 in register r of block db) times
+// scale, rounded to 16 bits (bf16 or fp16), stored to rows q_w .. q_w + 31 of
+// the buffer orr (row stride 256 bytes; rows past its end are dropped).  The
+// rows go through the wave's 4 KiB of LDS at stage (4 KiB aligned, nobody
+// else's while this runs), 16 at a time, so that each store writes whole
+// rows: lane L stores bytes [16 (L % 16), +16) of row L / 16 of a group of 4.
+// Stored straight from the accumulator layout, every row would arrive in 16
+// pieces of 16 bytes from 16 instructions; with all workgroups storing at once
+// those partial-line writes held the stores for thousands of cycles.
+template <bool BF16>
+__device__ __forceinline__ void store_o128_staged(__amdgpu_buffer_rsrc_t orr, int q_w, int lane, const f32x16& acc0,
+                                                  const f32x16& acc1, const f32x16& acc2, const f32x16& acc3,
+                                                  float scale, uint8_t* stage) {
+  using E = Elem<BF16>;
+  const int lr = lane & 31, lh = lane >> 5;
+  // Row r (of 16) at stage + 256 r, its 16-byte chunk c at 16 (c ^ r): the 16
+  // rows a half-wave writes, and the 4 rows a read covers, hit distinct banks.
+  // Chunk k = 4 db + i of row lr is d = 8 k .. 8 k + 7, its half lh from this
+  // lane (accumulator registers 4 i .. 4 i + 3 of block db).  The row, chunk
+  // and half occupy disjoint address bits, so every address is one per-lane
+  // base XOR an immediate; the empty asm keeps the compiler from hoisting
+  // per-lane addresses out of a caller's loop.
+  const uint32_t sbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)stage;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((lr >> 4) == half) {
+      const uint32_t r = lr & 15;
+      uint32_t wb = sbase | (256u * r + 16u * r + 8u * (uint32_t)lh);   // chunk k at wb ^ 16 k
+      asm volatile("" : "+v"(wb));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const f32x16& acc = db == 0 ? acc0 : db == 1 ? acc1 : db == 2 ? acc2 : acc3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 v;
+          v[0] = E::pack(acc[4 * i + 0] * scale, acc[4 * i + 1] * scale);
+          v[1] = E::pack(acc[4 * i + 2] * scale, acc[4 * i + 3] * scale);
+          *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(wb ^ (16u * (4 * db + i))) = v;
+        }
+      }
+    }
+    // lane L reads chunk c = L % 16 of row r = 4 g + L / 16, at
+    // (rb ^ 64 g) + 1024 g with rb = stage + 256 (L / 16) + 16 (c ^ (L / 16))
+    const uint32_t rr = (uint32_t)lane >> 4, c = (uint32_t)lane & 15;
+    uint32_t rb = sbase | (256u * rr + 16u * (c ^ rr));
+    asm volatile("" : "+v"(rb));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 x = lds_load_b128((rb ^ (64u * g)) + 1024u * g);
+      __builtin_amdgcn_raw_buffer_store_b128(x, orr, (uint32_t)((q_w + 16 * half + 4 * g + (int)rr) * 256 + 16 * (int)c),
+                                             0, 0);
+    }
+  }
+}
+
 // XOR swizzle of the 16-byte chunks of an unpadded LDS row of D 16-bit
 // elements (D = 128: 16 chunks, D = 64: 8 chunks).  With it, the 16 rows read
 // at one chunk by a 16-byte fragment read, and the 4 rows x 64 bytes of one

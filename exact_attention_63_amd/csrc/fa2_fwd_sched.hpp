@@ -47,9 +47,6 @@ constexpr int kSchedRows = 256;
 
 // LDS reads at a byte address (the kernel's only LDS allocation starts at the
 // address the pointer conversion gives; these take that address directly).
-__device__ __forceinline__ u32x4 lds_load_b128(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
-}
 __device__ __forceinline__ u32x2 lds_tr16_at(uint32_t addr) {
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)addr);
@@ -161,38 +158,25 @@ __device__ __forceinline__ void sched_loop(f32x16& acc0, f32x16& acc1, f32x16& a
 }
 
 // O = acc / l and LSE = (m + log2 l) ln 2 of the wave's rows q_w .. q_w + 31
-// (stores past the buffer are dropped).
+// (stores past the buffer are dropped); O through the wave's 4 KiB of LDS at
+// stage (store_o128_staged).
 template <bool BF16>
 __device__ __forceinline__ void sched_store(const Args& a, int bh, int q_w, int lane, const f32x16& acc0,
                                             const f32x16& acc1, const f32x16& acc2, const f32x16& acc3,
-                                            float m_run, float l_run) {
-  using E = Elem<BF16>;
-  constexpr int D = 128, KROW = 2 * D;
+                                            float m_run, float l_run, uint8_t* stage) {
+  constexpr int D = 128;
   const int N = a.N, lr = lane & 31, lh = lane >> 5;
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t orr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((uint16_t*)a.o + head_off), 0, head_bytes, kBufferWord3);
+      (void*)((uint16_t*)a.o + head_off), 0, (uint32_t)N * D * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t lsr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.lse + (size_t)bh * N), 0, (uint32_t)N * 4, kBufferWord3);
-  const int row = q_w + lr;
   const float l = sum_halves(l_run);
   const float inv = __builtin_amdgcn_rcpf(l);   // l >= 1: the row's largest p is 1
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const f32x16& acc = db == 0 ? acc0 : db == 1 ? acc1 : db == 2 ? acc2 : acc3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 v;
-      v[0] = E::pack(acc[4 * i + 0] * inv, acc[4 * i + 1] * inv);
-      v[1] = E::pack(acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
-      const int d = 32 * db + 8 * i + 4 * lh;
-      __builtin_amdgcn_raw_buffer_store_b64(v, orr, (uint32_t)(row * KROW + d * 2), 0, 0);
-    }
-  }
+  store_o128_staged<BF16>(orr, q_w, lane, acc0, acc1, acc2, acc3, inv, stage);
   if (lh == 0) {
     const float lse = (m_run + log2f(l)) * 0.69314718055994530942f;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lsr, (uint32_t)(row * 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), lsr, (uint32_t)((q_w + lr) * 4), 0, 0);
   }
 }
 
@@ -212,6 +196,7 @@ void fa2_fwd_sched_kernel(Args a) {
   static_assert(FA2_SCHED_REG_END <= 250, "the loop leaves VGPRs for the compiler");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];
+  __shared__ __attribute__((aligned(4096))) uint8_t ostage[8 * kStageBytes];   // output staging
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -356,7 +341,7 @@ void fa2_fwd_sched_kernel(Args a) {
     }
   }
 
-  sched_store<BF16>(a, bh, q_w, lane, acc0, acc1, acc2, acc3, m_run, l_run);
+  sched_store<BF16>(a, bh, q_w, lane, acc0, acc1, acc2, acc3, m_run, l_run, ostage + wave * kStageBytes);
 }
 
 // Persistent form for sequences of whole query blocks (N % 256 == 0), no
@@ -372,6 +357,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 void fa2_fwd_sched_persist_kernel(Args a) {
   constexpr int BR = kSchedRows, NS = 4, TSZ = 64 * 256;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * NS * TSZ];
+  __shared__ __attribute__((aligned(4096))) uint8_t ostage[8 * kStageBytes];   // output staging
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -419,7 +405,8 @@ void fa2_fwd_sched_persist_kernel(Args a) {
     f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
     float m_run, l_run;
     sched_loop<BF16>(acc0, acc1, acc2, acc3, m_run, l_run, q32, kr, vr, w, c, ntiles, nx, ntiles, ntiles);
-    sched_store<BF16>(a, bh, qblk * BR + wave * 32, lane, acc0, acc1, acc2, acc3, m_run, l_run);
+    sched_store<BF16>(a, bh, qblk * BR + wave * 32, lane, acc0, acc1, acc2, acc3, m_run, l_run,
+                      ostage + wave * kStageBytes);
     if (nxt < 0) break;
     bh = nxt / nqb;
     qblk = nxt % nqb;
